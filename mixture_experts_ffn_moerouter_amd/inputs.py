@@ -1,0 +1,214 @@
+"""Seeded synthetic inputs for the routed MoE FFN: workload shapes and generators.
+
+This module holds none of the method's arithmetic. It feeds the same tensors to the GPU
+library and to the CPU oracle, so it imports neither.
+
+Generator: a counter-based SplitMix64 stream (Steele, Lea and Flood, "Fast splittable
+pseudorandom number generators", OOPSLA 2014: state step 0x9E3779B97F4A7C15 and the
+"mix64" finaliser with multipliers 0xBF58476D1CE4E5B9 / 0x94D049BB133111EB). Element i
+of the tensor with stream id `stream` under `seed` takes the 64-bit word
+    mix64(key + (c + 1) * 0x9E3779B97F4A7C15),   key = mix64(seed * 0x9E3779B97F4A7C15 + stream)
+for counter c; the top 53 bits give a uniform u in [0, 1). Normals use the Box-Muller
+transform (Box and Muller, 1958) on counters 2i and 2i+1:
+    n = sqrt(-2 ln(1 - u_2i)) * cos(2 pi u_2i+1).
+Values are computed in float64 and then cast to the tensor dtype. Any element can be
+regenerated alone, and torch integer ops wrap identically on CPU and GPU.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import torch
+
+_GOLDEN = 0x9E3779B97F4A7C15
+_M1 = 0xBF58476D1CE4E5B9
+_M2 = 0x94D049BB133111EB
+_MASK64 = (1 << 64) - 1
+_CHUNK = 1 << 24
+
+# Stream id of every generated tensor.
+STREAMS = {
+    "hidden": 0, "logits": 1, "w_gate_up": 2, "w_down": 3, "b_gate_up": 4, "b_down": 5,
+    "correction_bias": 6, "shared_w_gate_up": 7, "shared_w_down": 8, "expert_ids": 9,
+}
+
+
+def _s64(v: int) -> int:
+    v &= _MASK64
+    return v - (1 << 64) if v >= (1 << 63) else v
+
+
+def mix64_int(z: int) -> int:
+    """SplitMix64 finaliser on a Python int (reference for the tensor version)."""
+    z &= _MASK64
+    z = ((z ^ (z >> 30)) * _M1) & _MASK64
+    z = ((z ^ (z >> 27)) * _M2) & _MASK64
+    return z ^ (z >> 31)
+
+
+def _shr(z: torch.Tensor, s: int) -> torch.Tensor:
+    return (z >> s) & ((1 << (64 - s)) - 1)  # logical shift of an int64 tensor
+
+
+def _mix64(z: torch.Tensor) -> torch.Tensor:
+    z = (z ^ _shr(z, 30)) * _s64(_M1)
+    z = (z ^ _shr(z, 27)) * _s64(_M2)
+    return z ^ _shr(z, 31)
+
+
+def stream_key(seed: int, stream: int) -> int:
+    return mix64_int(seed * _GOLDEN + stream)
+
+
+def uniform_words(key: int, counters: torch.Tensor) -> torch.Tensor:
+    """64-bit words (as int64) of the stream at the given int64 counters."""
+    return _mix64(_s64(key) + (counters + 1) * _s64(_GOLDEN))
+
+
+def _uniform(key: int, counters: torch.Tensor) -> torch.Tensor:
+    return _shr(uniform_words(key, counters), 11).to(torch.float64) * (2.0 ** -53)
+
+
+def _fill(out: torch.Tensor, key: int, kind: str, a: float, b: float) -> torch.Tensor:
+    flat = out.view(-1)
+    n = flat.numel()
+    dev = out.device
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        i = torch.arange(lo, hi, dtype=torch.int64, device=dev)
+        if kind == "normal":
+            u1 = _uniform(key, 2 * i)
+            u2 = _uniform(key, 2 * i + 1)
+            v = torch.sqrt(-2.0 * torch.log1p(-u1)) * torch.cos((2.0 * math.pi) * u2)
+            v = a + b * v
+        elif kind == "uniform":
+            v = a + (b - a) * _uniform(key, i)
+        else:
+            raise ValueError(kind)
+        flat[lo:hi] = v.to(out.dtype)
+    return out
+
+
+def normal(shape, std: float, *, seed: int, stream: int, dtype=torch.float32,
+           device="cpu", mean: float = 0.0) -> torch.Tensor:
+    out = torch.empty(shape, dtype=dtype, device=device)
+    return _fill(out, stream_key(seed, stream), "normal", mean, std)
+
+
+def uniform(shape, lo: float, hi: float, *, seed: int, stream: int, dtype=torch.float32,
+            device="cpu") -> torch.Tensor:
+    out = torch.empty(shape, dtype=dtype, device=device)
+    return _fill(out, stream_key(seed, stream), "uniform", lo, hi)
+
+
+def random_expert_ids(T: int, K: int, E: int, *, seed: int, device="cpu") -> torch.Tensor:
+    """[T,K] int32 hash-routing ids, K distinct experts per token (a seeded permutation)."""
+    key = stream_key(seed, STREAMS["expert_ids"])
+    i = torch.arange(T * E, dtype=torch.int64, device=device)
+    r = _shr(uniform_words(key, i), 1).view(T, E)
+    return torch.argsort(r, dim=1)[:, :K].to(torch.int32)
+
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    """One workload: model shapes, routing and activation options, input distributions."""
+    name: str
+    T: int
+    H: int
+    E: int
+    F: int
+    K: int
+    scoring: str = "softmax"
+    renormalize: bool = True
+    rsf: float = 1.0
+    G: int = 1
+    TG: int = 1
+    act: str = "silu_and_mul"
+    dtype: str = "bf16"
+    w_std: float = 0.02
+    x_std: float = 1.0
+    logit_std: float = 1.0
+    bias_std: Optional[float] = None            # b_gate_up / b_down ~ N(0, bias_std)
+    correction_bias: Optional[tuple] = None     # (lo, hi) uniform
+    F_s: int = 0                                # shared expert width; 0 = none
+    local_expert_start: int = 0
+    local_expert_count: Optional[int] = None
+    router_probs_dtype: Optional[str] = None
+    hash_routing: bool = False
+    notes: str = field(default="", compare=False)
+
+    @property
+    def R(self) -> int:
+        return self.T * self.K
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DT[self.dtype]
+
+    def with_(self, **kw) -> "MoEConfig":
+        return replace(self, **kw)
+
+
+# The workloads. Shapes follow the model families the pages name: Qwen3 softmax
+# routing; gpt-oss interleaved swigluoai with expert biases; DeepSeek-V3 sigmoid routing
+# with correction bias, 8 groups / 4 kept, scaling 2.5 and a shared expert.
+CONFIGS = {
+    "tiny_fp32": MoEConfig("tiny_fp32", T=64, H=128, E=8, F=64, K=2, dtype="f32",
+                           w_std=0.05),
+    "qwen3_bf16": MoEConfig("qwen3_bf16", T=4096, H=2048, E=128, F=768, K=8),
+    "gptoss_bf16": MoEConfig("gptoss_bf16", T=2048, H=2880, E=128, F=2880, K=4,
+                             act="swigluoai", bias_std=0.01),
+    "dsv3_bf16": MoEConfig("dsv3_bf16", T=4096, H=7168, E=256, F=2048, K=8,
+                           scoring="sigmoid", rsf=2.5, G=8, TG=4,
+                           correction_bias=(-0.1, 0.1), F_s=2048),
+    "decode_dsv3_bf16": MoEConfig("decode_dsv3_bf16", T=16, H=7168, E=256, F=2048, K=8,
+                                  scoring="sigmoid", rsf=2.5, G=8, TG=4,
+                                  correction_bias=(-0.1, 0.1)),
+    # Router-only pass: sqrt_softplus scoring, plain top-k, one expert-parallel slice.
+    "router_ep_f16": MoEConfig("router_ep_f16", T=16, H=0, E=256, F=0, K=8,
+                               scoring="sqrt_softplus", local_expert_start=64,
+                               local_expert_count=64, router_probs_dtype="f16"),
+}
+
+
+def make_router_inputs(cfg: MoEConfig, *, seed: int = 0, device="cpu") -> dict:
+    d = {"logits": normal((cfg.T, cfg.E), cfg.logit_std, seed=seed,
+                          stream=STREAMS["logits"], dtype=torch.float32, device=device)}
+    if cfg.correction_bias is not None:
+        lo, hi = cfg.correction_bias
+        d["correction_bias"] = uniform((cfg.E,), lo, hi, seed=seed,
+                                       stream=STREAMS["correction_bias"],
+                                       dtype=torch.float32, device=device)
+    if cfg.hash_routing:
+        d["expert_ids"] = random_expert_ids(cfg.T, cfg.K, cfg.E, seed=seed, device=device)
+    return d
+
+
+def make_inputs(cfg: MoEConfig, *, seed: int = 0, device="cpu") -> dict:
+    """All input tensors of one workload, generated directly on `device`."""
+    dt = cfg.torch_dtype
+    d = make_router_inputs(cfg, seed=seed, device=device)
+    d["hidden"] = normal((cfg.T, cfg.H), cfg.x_std, seed=seed, stream=STREAMS["hidden"],
+                         dtype=dt, device=device)
+    d["w_gate_up"] = normal((cfg.E, 2 * cfg.F, cfg.H), cfg.w_std, seed=seed,
+                            stream=STREAMS["w_gate_up"], dtype=dt, device=device)
+    d["w_down"] = normal((cfg.E, cfg.H, cfg.F), cfg.w_std, seed=seed,
+                         stream=STREAMS["w_down"], dtype=dt, device=device)
+    if cfg.bias_std is not None:
+        d["b_gate_up"] = normal((cfg.E, 2 * cfg.F), cfg.bias_std, seed=seed,
+                                stream=STREAMS["b_gate_up"], dtype=dt, device=device)
+        d["b_down"] = normal((cfg.E, cfg.H), cfg.bias_std, seed=seed,
+                             stream=STREAMS["b_down"], dtype=dt, device=device)
+    if cfg.F_s:
+        d["shared_w_gate_up"] = normal((2 * cfg.F_s, cfg.H), cfg.w_std, seed=seed,
+                                       stream=STREAMS["shared_w_gate_up"], dtype=dt,
+                                       device=device)
+        d["shared_w_down"] = normal((cfg.H, cfg.F_s), cfg.w_std, seed=seed,
+                                    stream=STREAMS["shared_w_down"], dtype=dt,
+                                    device=device)
+    return d

@@ -1,0 +1,468 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each pin_* function raises AssertionError when the oracle disagrees with a closed form,
+a brute-force enumeration, an identity the pages fix, or an independent library routine.
+They reach the oracle only through the module object `O`, so test_oracle_mutants.py can
+plant a mistake in one oracle function and check that some pin catches it.
+"""
+import itertools
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+
+import numpy as np
+import torch
+
+import oracle.moe_oracle as O
+
+getcontext().prec = 60
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                     "page_constants.json")))
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _f32(x):
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _D(x):
+    return Decimal(float(x))
+
+
+def _dsig(x):
+    return 1 / (1 + (-x).exp())
+
+
+# ------------------------------------------------------------------- rounding
+def pin_round_f32_f16():
+    r = _rng(1)
+    x = np.concatenate([
+        r.standard_normal(4000) * 10.0 ** r.integers(-45, 39, 4000),
+        r.standard_normal(500) * 1e-41, np.array([3.5e38, 3.4028235e38, 3.4028236e38, -7e45]),
+    ])
+    assert np.array_equal(O.round_to(x, "f32"), x.astype(np.float32).astype(np.float64))
+    y = np.concatenate([r.standard_normal(4000) * 10.0 ** r.integers(-9, 5, 4000),
+                        np.array([65504.0, 65519.99, 65520.0, 1e-8, 6e-8, -3e-5])])
+    assert np.array_equal(O.round_to(y, "f16"), y.astype(np.float16).astype(np.float64))
+
+
+def _all_bf16_values():
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    v = bits.view(np.float32).astype(np.float64)
+    v = v[np.isfinite(v)]
+    v = np.unique(v)          # sorted, -0.0 merged with 0.0
+    return v
+
+
+def pin_round_bf16_bruteforce():
+    vals = _all_bf16_values()
+    mant_odd = {}
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    fv = (bits << 16).view(np.float32).astype(np.float64)
+    for b, v in zip(bits, fv):
+        if np.isfinite(v):
+            mant_odd[float(v)] = bool(b & 1)
+    r = _rng(2)
+    x = np.concatenate([r.standard_normal(3000) * 10.0 ** r.integers(-40, 38, 3000),
+                        # exact ties between neighbours
+                        (vals[1000:1200] + vals[1001:1201]) / 2.0])
+    got = O.round_to(x, "bf16")
+    for xi, gi in zip(x, got):
+        j = np.searchsorted(vals, xi)
+        lo, hi = vals[max(j - 1, 0)], vals[min(j, vals.size - 1)]
+        dlo, dhi = abs(xi - lo), abs(hi - xi)
+        if dlo < dhi:
+            want = lo
+        elif dhi < dlo:
+            want = hi
+        else:
+            want = hi if not mant_odd[float(hi)] else lo
+        assert gi == want, (xi, gi, want)
+    # independent library: torch's float32 -> bfloat16 cast (round to nearest even)
+    x32 = r.standard_normal(20000).astype(np.float32)
+    t = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_to(x32.astype(np.float64), "bf16"), t)
+
+
+# ------------------------------------------------------------------- scoring
+def pin_scores_closed_forms():
+    zs = [0.0, 1.0, -1.0, 20.0, -20.0, 3.5, -0.75]
+    s = O.scores(np.array([zs]), "sqrt_softplus")[0]
+    for z, v in zip(zs, s):
+        want = (1 + _D(z).exp()).ln().sqrt()
+        assert abs(_D(v) - want) <= Decimal("1e-15") * want, (z, v, want)
+    assert abs(s[0] - math.sqrt(math.log(2.0))) < 1e-15
+    g = O.scores(np.array([zs]), "sigmoid")[0]
+    for z, v in zip(zs, g):
+        want = _dsig(_D(z))
+        assert abs(_D(v) - want) <= Decimal("1e-15") * want, (z, v)
+    assert g[0] == 0.5
+    r = _rng(3)
+    z = r.standard_normal((5, 9)) * 3
+    sm = O.scores(z, "softmax")
+    for row_z, row_s in zip(z, sm):
+        den = sum(_D(v).exp() for v in row_z)
+        for v, p in zip(row_z, row_s):
+            want = _D(v).exp() / den
+            assert abs(_D(p) - want) <= Decimal("1e-14") * want
+    assert np.allclose(sm.sum(axis=1), 1.0, atol=1e-15, rtol=0)
+    assert np.allclose(O.scores(z + 100.0, "softmax"), sm, atol=0, rtol=1e-13)
+
+
+# ------------------------------------------------------------------- selection
+def _key(u, e):
+    return (-u, e)
+
+
+def _brute_select(u, K, G=1, TG=1, biased=False):
+    """Brute force: enumerate every TG-subset of groups and every K-subset of experts; the
+    answer is the unique subset whose members all precede every non-member under
+    (value descending, index ascending)."""
+    E = u.size
+    eligible = list(range(E))
+    if G > 1:
+        gsz = E // G
+        gs = []
+        for g in range(G):
+            mem = u[g * gsz:(g + 1) * gsz]
+            if biased and gsz >= 2:
+                best = max(O.round_to(mem[i] + mem[j], "f32")
+                           for i in range(gsz) for j in range(gsz) if i != j)
+            else:
+                best = max(mem)
+            gs.append(float(best))
+        kept = None
+        for sub in itertools.combinations(range(G), TG):
+            rest = [g for g in range(G) if g not in sub]
+            if all(_key(gs[a], a) < _key(gs[b], b) for a in sub for b in rest):
+                assert kept is None
+                kept = sub
+        eligible = [e for e in range(E) if e // gsz in kept]
+    chosen = None
+    for sub in itertools.combinations(eligible, K):
+        rest = [e for e in eligible if e not in sub]
+        if all(_key(u[a], a) < _key(u[b], b) for a in sub for b in rest):
+            assert chosen is None
+            chosen = sub
+    return sorted(chosen, key=lambda e: _key(u[e], e))
+
+
+def pin_select_bruteforce():
+    r = _rng(4)
+    cases = [(8, 2, 1, 1, False), (8, 3, 1, 1, True), (16, 3, 4, 2, False),
+             (16, 3, 4, 2, True), (12, 4, 3, 2, True), (8, 2, 8, 3, True)]
+    for E, K, G, TG, biased in cases:
+        for trial in range(25):
+            logits = _f32(r.standard_normal((1, E)))
+            bias = _f32(r.uniform(-0.1, 0.1, E)) if biased else None
+            scoring = "sigmoid" if biased else ["softmax", "sigmoid", "sqrt_softplus"][trial % 3]
+            s = O.scores(logits, scoring)
+            sel, _, _ = O.select_experts(s, K, bias, G, TG)
+            u = _f32(s[0]) if bias is None else O.round_to(_f32(s[0]) + bias, "f32")
+            assert list(sel[0]) == _brute_select(u, K, G, TG, biased), (E, K, G, TG, trial)
+
+
+def pin_select_ties():
+    # all-equal logits: ids 0..K-1, weights 1/K * rsf
+    res = O.route(np.zeros((2, 8)), 3, "softmax", True, 2.5)
+    assert res.topk_ids.tolist() == [[0, 1, 2], [0, 1, 2]]
+    assert np.allclose(res.topk_weights, 2.5 / 3, rtol=1e-7)
+    # pairwise-equal keys go to the lower index
+    z = np.array([[0.1, 0.9, 0.3, 0.9, 0.3, -1.0]])
+    assert O.route(z, 3, "sigmoid").topk_ids.tolist() == [[1, 3, 2]]
+    # equal group scores: the lower group is kept
+    z = np.array([[0.5, 0.2, 0.2, 0.5, 0.0, 0.0]])
+    res = O.route(z, 2, "sigmoid", num_expert_group=3, topk_group=1,
+                  correction_bias=np.zeros(6))
+    assert res.topk_ids.tolist() == [[0, 1]]
+    # negative zero equals zero: index decides
+    assert list(O.ranked(np.array([-0.0, 0.0, -0.0]))) == [0, 1, 2]
+
+
+def pin_group_score_rule():
+    # with a bias the group score is the sum of the two best biased scores, not the max
+    z = np.zeros((1, 8))
+    bias = np.array([0.30, 0.0, 0.0, 0.0, 0.20, 0.20, 0.0, 0.0])
+    res = O.route(z, 2, "sigmoid", num_expert_group=2, topk_group=1, correction_bias=bias)
+    assert res.topk_ids.tolist() == [[4, 5]]          # 0.7+0.7 > 0.8+0.5
+    # selection uses biased keys, weights use unbiased scores
+    assert np.allclose(res.wn, [[0.5, 0.5]])
+    # without a bias the group score is the best score
+    z2 = np.array([[2.0, -5, -5, -5, 1.5, 1.4, 1.3, 1.2]])
+    assert O.route(z2, 2, "sigmoid", num_expert_group=2,
+                   topk_group=1).topk_ids.tolist() == [[0, 1]]
+
+
+# ------------------------------------------------------------------- weights
+def pin_weights_closed_forms():
+    r = _rng(5)
+    z = _f32(r.standard_normal((6, 10)))
+    res = O.route(z, 4, "softmax", True, 1.7)
+    assert np.allclose(res.topk_weights.sum(axis=1), 1.7, rtol=1e-6)
+    for t in range(6):
+        sub = z[t, res.topk_ids[t]]
+        want = np.exp(sub) / np.exp(sub).sum()      # softmax over the chosen logits alone
+        assert np.allclose(res.wn[t], want, rtol=1e-13)
+    res2 = O.route(z, 4, "sigmoid", False, 1.0)
+    assert np.allclose(res2.wn, 1 / (1 + np.exp(-np.take_along_axis(z, res2.topk_ids, 1))),
+                       rtol=1e-14)
+    # hash routing: the given experts, normalized affinities, bias ignored
+    ids = np.array([[3, 1], [0, 9], [5, 4], [2, 8], [7, 6], [9, 0]])
+    res3 = O.route(z, 2, "sigmoid", True, 1.0, correction_bias=np.full(10, 5.0),
+                   expert_ids=ids)
+    assert res3.topk_ids.tolist() == ids.tolist()
+    sg = 1 / (1 + np.exp(-np.take_along_axis(z, ids, 1)))
+    assert np.allclose(res3.wn, sg / sg.sum(axis=1, keepdims=True), rtol=1e-14)
+
+
+# ------------------------------------------------------------------- EP router outputs
+def pin_ep_outputs():
+    fills = GOLDEN["router_probs_fill"]
+    r = _rng(6)
+    z = _f32(r.standard_normal((40, 16)))
+    for dt in ("f32", "bf16", "f16"):
+        full = O.route(z, 4, "softmax", True, 2.0, router_probs_dtype=dt)
+        assert np.allclose(full.weight_scale, 2.0, rtol=2e-3)  # full slice: W_local = 1
+        res = O.route(z, 4, "softmax", True, 2.0, local_expert_start=4,
+                      local_expert_count=6, router_probs_dtype=dt)
+        fill = O.round_to(fills[dt], dt)
+        for t in range(40):
+            local = [(k, e) for k, e in enumerate(res.topk_ids[t]) if 4 <= e < 10]
+            row = res.router_probs[t]
+            if not local:
+                assert res.weight_scale[t] == 0.0
+                assert np.all(row == fill)
+                continue
+            sm = np.exp(row - row.max())
+            sm = sm / sm.sum()
+            rec = res.weight_scale[t] * sm                 # what the consumer rebuilds
+            want = np.zeros(6)
+            for k, e in local:
+                want[e - 4] = res.topk_weights[t, k]
+            tol = {"f32": 1e-6, "bf16": 2e-2, "f16": 2e-3}[dt]
+            assert np.allclose(rec, want, rtol=tol, atol=tol * 1e-2), (dt, t)
+            mask = np.ones(6, bool)
+            mask[[e - 4 for _, e in local]] = False
+            assert np.all(row[mask] == fill)
+    assert O.round_to(-1e30, "f16") == -np.inf        # why float16 needs its own fill
+    assert O.round_to(fills["f16"], "f16") == -1e4
+    # fake multi-rank: scale_r * softmax(row_r), summed over ranks, is the global weight
+    res_all = O.route(z, 4, "softmax", True, 2.0)
+    total = np.zeros((40, 16))
+    for rank in range(4):
+        rr = O.route(z, 4, "softmax", True, 2.0, local_expert_start=4 * rank,
+                     local_expert_count=4, router_probs_dtype="f32")
+        row = rr.router_probs
+        sm = np.exp(row - row.max(axis=1, keepdims=True))
+        sm = sm / sm.sum(axis=1, keepdims=True)
+        total[:, 4 * rank:4 * rank + 4] = rr.weight_scale[:, None] * sm
+    want = np.zeros((40, 16))
+    np.put_along_axis(want, res_all.topk_ids, res_all.topk_weights, axis=1)
+    assert np.allclose(total, want, rtol=1e-6, atol=1e-7)
+
+
+# ------------------------------------------------------------------- SwiGLU
+def _dswiglu(g, l, alpha, beta, limit):
+    g, l = _D(g), _D(l)
+    if limit > 0:
+        g = min(g, _D(limit))
+        l = max(min(l, _D(limit)), -_D(limit))
+    return g * _dsig(_D(alpha) * g) * (l + _D(beta))
+
+
+def pin_swiglu_closed_forms():
+    oai = GOLDEN["swigluoai"]
+    assert O.ACTIVATIONS["swigluoai"] == ("interleaved", oai["alpha"], oai["beta"],
+                                          oai["limit"])
+    assert O.ACTIVATIONS["silu_and_mul"][0] == GOLDEN["silu_and_mul"]["layout"]
+    cases = [((1.0, 1.0), (1.0, 0.0, 0.0), 0.7310585786300049),
+             ((-2.0, 3.0), (1.0, 0.0, 0.0), -0.7152175321327052),
+             ((10.0, 10.0), (1.702, 1.0, 7.0), 55.99962502642654),
+             ((-10.0, -10.0), (1.702, 1.0, 7.0), 2.434776776913187e-06),
+             ((0.5, -0.25), (1.702, 1.0, 7.0), 0.2627913274547851),
+             ((10.0, 10.0), (1.702, 1.0, 0.0), 109.99999553624258),
+             ((10.0, 10.0), (1.702, 1.0, -1.0), 109.99999553624258),
+             ((3.0, -9.0), (1.0, 0.5, 7.0), None), ((-3.0, 9.0), (0.7, -0.5, 2.0), None)]
+    for (g, l), (a, b, lim), printed in cases:
+        got = float(O.swiglu(g, l, a, b, lim))
+        want = _dswiglu(g, l, a, b, lim)
+        assert abs(_D(got) - want) <= Decimal("1e-15") * abs(want), (g, l, got, want)
+        if printed is not None:
+            assert abs(got - printed) <= 4e-16 * abs(printed)
+
+
+def _torch_dense_gated(x, wg, wu, wd, act_round):
+    xt = torch.from_numpy(np.asarray(x, np.float64))
+    a = torch.nn.functional.silu(xt @ torch.from_numpy(wg).T) * (xt @ torch.from_numpy(wu).T)
+    a = act_round(a)
+    return (a @ torch.from_numpy(wd).T).numpy()
+
+
+def pin_expert_mlp_dense_special_case():
+    r = _rng(7)
+    T, H, F = 9, 24, 10
+    x = _f32(r.standard_normal((T, H)))
+    wgu = _f32(r.standard_normal((1, 2 * F, H)) * 0.2)
+    wd = _f32(r.standard_normal((1, H, F)) * 0.2)
+    z = np.zeros((T, 1))
+    out = O.moe_ffn_forward(x, z, wgu, wd, top_k=1, renormalize=True, dtype="f32")["out"]
+    ref = _torch_dense_gated(x, wgu[0, :F], wgu[0, F:], wd[0],
+                             lambda a: a.to(torch.float32).to(torch.float64))
+    assert np.allclose(out, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    sh = O.shared_expert_mlp(x, wgu[0], wd[0], "f32")
+    assert np.allclose(sh, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    shb = O.shared_expert_mlp(x, wgu[0], wd[0], "bf16")
+    refb = _torch_dense_gated(x, wgu[0, :F], wgu[0, F:], wd[0],
+                              lambda a: a.to(torch.bfloat16).to(torch.float64))
+    assert np.allclose(shb, refb, rtol=1e-2, atol=1e-3)
+
+
+def pin_layout_and_bias_identities():
+    r = _rng(8)
+    T, H, F = 7, 16, 6
+    x = _f32(r.standard_normal((T, H)))
+    w_st = _f32(r.standard_normal((2 * F, H)) * 0.3)
+    wd = _f32(r.standard_normal((H, F)) * 0.3)
+    # stacked -> interleaved row permutation gives the same MLP
+    perm = np.empty(2 * F, dtype=np.int64)
+    perm[0::2] = np.arange(F)
+    perm[1::2] = F + np.arange(F)
+    a1, y1 = O.expert_mlp(x, w_st, wd, act=("stacked", 1.3, 0.2, 1.5), act_dtype="f64")
+    a2, y2 = O.expert_mlp(x, w_st[perm], wd, act=("interleaved", 1.3, 0.2, 1.5),
+                          act_dtype="f64")
+    assert np.allclose(a1, a2, rtol=1e-14) and np.allclose(y1, y2, rtol=1e-13)
+    # gate rows really are the gate: swapping halves changes the result
+    a3, _ = O.expert_mlp(x, np.concatenate([w_st[F:], w_st[:F]]), wd, act_dtype="f64")
+    a4, _ = O.expert_mlp(x, w_st, wd, act_dtype="f64")
+    g, u = x @ w_st[:F].T, x @ w_st[F:].T
+    assert np.allclose(a4, g / (1 + np.exp(-g)) * u, rtol=1e-13)
+    assert not np.allclose(a3, a4)
+    # a bias equals one more input column holding 1 (augmentation identity)
+    bgu = _f32(r.standard_normal(2 * F) * 0.5)
+    bd = _f32(r.standard_normal(H) * 0.5)
+    xa = np.concatenate([x, np.ones((T, 1))], axis=1)
+    wa = np.concatenate([w_st, bgu[:, None]], axis=1)
+    a5, y5 = O.expert_mlp(x, w_st, wd, bgu, bd, act="swigluoai", act_dtype="f64")
+    a6, y6 = O.expert_mlp(xa, wa, wd, act="swigluoai", act_dtype="f64")
+    assert np.allclose(a5, a6, rtol=1e-13)
+    assert np.allclose(y5, y6 + bd[None, :], rtol=1e-13)
+
+
+# ------------------------------------------------------------------- stages
+def pin_grouped_gemm_bruteforce():
+    r = _rng(9)
+    E, N, K = 3, 5, 7
+    off = np.array([0, 4, 4, 9])
+    a = r.standard_normal((9, K))
+    b = r.standard_normal((E, N, K))
+    bias = r.standard_normal((E, N))
+    out = O.grouped_gemm(a, b, off, bias, "f64")
+    for e in range(E):
+        for m in range(off[e], off[e + 1]):
+            for n in range(N):
+                want = math.fsum(a[m, k] * b[e, n, k] for k in range(K)) + bias[e, n]
+                assert abs(out[m, n] - want) < 1e-12
+    b2 = r.standard_normal((E, 2 * 3, K))
+    act = O.grouped_gemm_act(a, b2, off, "swigluoai", None, "f64")
+    for e in range(E):
+        for m in range(off[e], off[e + 1]):
+            for j in range(3):
+                g = math.fsum(a[m, k] * b2[e, 2 * j, k] for k in range(K))
+                u = math.fsum(a[m, k] * b2[e, 2 * j + 1, k] for k in range(K))
+                want = float(_dswiglu(g, u, 1.702, 1.0, 7.0))
+                assert abs(act[m, j] - want) < 1e-12 * max(1.0, abs(want))
+
+
+def pin_permute_invariants():
+    r = _rng(10)
+    for T, K, E in [(13, 3, 5), (40, 2, 9), (1, 1, 1), (0, 2, 4)]:
+        ids = np.stack([r.permutation(E)[:K] for _ in range(T)]) if T else \
+            np.zeros((0, K), np.int64)
+        off, srt, pos = O.permute(ids, E)
+        flat = ids.reshape(-1)
+        assert sorted(srt.tolist()) == list(range(T * K))
+        assert all(flat[srt[i]] <= flat[srt[i + 1]] for i in range(T * K - 1))
+        cnt = [0] * E
+        for e in flat:
+            cnt[e] += 1
+        assert off.tolist() == [sum(cnt[:e]) for e in range(E + 1)]
+        assert all(pos[srt[i]] == i for i in range(T * K))
+        for e in range(E):
+            seg = srt[off[e]:off[e + 1]].tolist()
+            assert seg == sorted(seg) and all(flat[x] == e for x in seg)
+
+
+def pin_combine_bruteforce():
+    r = _rng(11)
+    T, K, H = 5, 3, 4
+    y = r.standard_normal((T * K, H))
+    w = r.standard_normal((T, K))
+    pos = r.permutation(T * K)
+    out = O.combine(y, w, pos, 1.5, "f64")
+    for t in range(T):
+        for h in range(H):
+            want = 1.5 * math.fsum(w[t, k] * y[pos[t * K + k], h] for k in range(K))
+            assert abs(out[t, h] - want) < 1e-13
+
+
+def pin_ffn_soft_mixture():
+    """K = E with softmax and no renormalization is the dense soft mixture
+    sum_e p_e f_e(x); the routed path must reproduce it."""
+    r = _rng(12)
+    T, H, E, F = 6, 12, 4, 5
+    x = _f32(r.standard_normal((T, H)))
+    z = _f32(r.standard_normal((T, E)))
+    wgu = _f32(r.standard_normal((E, 2 * F, H)) * 0.3)
+    wd = _f32(r.standard_normal((E, H, F)) * 0.3)
+    bgu = _f32(r.standard_normal((E, 2 * F)) * 0.1)
+    bd = _f32(r.standard_normal((E, H)) * 0.1)
+    for act in ("silu_and_mul", "swigluoai"):
+        got = O.moe_ffn_forward(x, z, wgu, wd, top_k=E, renormalize=False, act=act,
+                                dtype="f32", b_gate_up=bgu, b_down=bd)["out"]
+        p = np.exp(z - z.max(1, keepdims=True))
+        p = p / p.sum(1, keepdims=True)
+        want = np.zeros((T, H))
+        for t in range(T):
+            for e in range(E):
+                layout, al, be, li = O.ACTIVATIONS[act]
+                h = wgu[e] @ x[t] + bgu[e]
+                g, u = (h[:F], h[F:]) if layout == "stacked" else (h[0::2], h[1::2])
+                if li > 0:
+                    g, u = np.minimum(g, li), np.clip(u, -li, li)
+                a = _f32(g / (1 + np.exp(-al * g)) * (u + be))
+                want[t] += _f32(p[t, e]) * (wd[e] @ a + bd[e])
+        assert np.allclose(got, want, rtol=2e-6, atol=1e-6), act
+
+
+def pin_ffn_token_subset():
+    r = _rng(13)
+    T, H, E, F, K = 20, 8, 6, 4, 2
+    x = _f32(r.standard_normal((T, H)))
+    z = _f32(r.standard_normal((T, E)))
+    wgu = _f32(r.standard_normal((E, 2 * F, H)) * 0.3)
+    wd = _f32(r.standard_normal((E, H, F)) * 0.3)
+    kw = dict(top_k=K, scoring="sigmoid", renormalize=True, routed_scaling_factor=2.5,
+              num_expert_group=3, topk_group=2, correction_bias=_f32(r.uniform(-.1, .1, E)),
+              dtype="bf16")
+    full = O.moe_ffn_forward(x, z, wgu, wd, **kw)["out"]
+    sub = O.moe_ffn_forward(x, z, wgu, wd, tokens=np.array([17, 3, 9]), **kw)["out"]
+    assert np.array_equal(sub, full[[17, 3, 9]])
+
+
+def pin_dispatch_rule():
+    d = GOLDEN["indexed_dispatch"]
+    assert d["H_multiple"] == 128 and d["F_multiple"] == 256
+    assert O.indexed_backend_applies(16, 8, 256, 7168, 2048, "silu_and_mul", False)
+    assert not O.indexed_backend_applies(4096, 8, 128, 2048, 768, "silu_and_mul", False)
+    assert not O.indexed_backend_applies(16, 4, 128, 2880, 2880, "swigluoai", True)
+    assert O.indexed_backend_applies(64, 8, 256, 7168, 2048, "silu_and_mul", False)
+    assert not O.indexed_backend_applies(65, 8, 256, 7168, 2048, "silu_and_mul", False)
+    assert not O.indexed_backend_applies(16, 8, 256, 7168 + 64, 2048, "silu_and_mul", False)
+    assert not O.indexed_backend_applies(16, 8, 256, 7168, 2048 + 128, "silu_and_mul", False)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

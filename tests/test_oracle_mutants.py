@@ -1,0 +1,153 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that a pin catches each.
+
+A pin suite that still passes with a mistake planted would not be pinning that part.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as O
+import oracle_pins as P
+
+
+def _swiglu_two_sided_gate(g, l, alpha=1.0, beta=0.0, limit=0.0):
+    g = np.asarray(g, np.float64)
+    l = np.asarray(l, np.float64)
+    if limit > 0:
+        g = np.clip(g, -limit, limit)
+        l = np.clip(l, -limit, limit)
+    return g * O.sigmoid(alpha * g) * (l + beta)
+
+
+def _swiglu_no_disable(g, l, alpha=1.0, beta=0.0, limit=0.0):
+    g = np.minimum(np.asarray(g, np.float64), limit if limit > 0 else 7.0)
+    l = np.clip(np.asarray(l, np.float64), -7.0, 7.0) if limit <= 0 else np.clip(l, -limit, limit)
+    return g * O.sigmoid(alpha * g) * (l + beta)
+
+
+def _split_swapped(h, layout):
+    g, u = _orig_split(h, layout)
+    return u, g
+
+
+def _ranked_high_index(values):
+    v = np.asarray(values, np.float64)
+    return np.lexsort((-np.arange(v.size), -v))
+
+
+def _weights_rsf_twice(s, sel, renormalize, rsf):
+    wn, w = _orig_weights(s, sel, renormalize, rsf)
+    return wn, w * rsf
+
+
+def _weights_biased(s, sel, renormalize, rsf):
+    # renormalize by the sum over all experts instead of the chosen ones
+    w = np.take_along_axis(np.asarray(s, np.float64), np.asarray(sel), axis=1)
+    wn = w / np.asarray(s).sum(axis=1, keepdims=True) if renormalize else w
+    return wn, wn * rsf
+
+
+def _combine_transposed(y, topk_weights, route_pos, scale=1.0, out_dtype="f32"):
+    w = np.asarray(topk_weights, np.float64)
+    T, K = w.shape
+    pos = np.asarray(route_pos).reshape(K, T).T
+    out = np.zeros((T, np.asarray(y).shape[1]))
+    for k in range(K):
+        out += w[:, k:k + 1] * np.asarray(y)[pos[:, k]]
+    return O.round_to(scale * out, out_dtype)
+
+
+def _expert_mlp_no_down_bias(x, w_gate_up, w_down, b_gate_up=None, b_down=None,
+                             act="silu_and_mul", act_dtype="f32"):
+    return _orig_expert_mlp(x, w_gate_up, w_down, b_gate_up, None, act, act_dtype)
+
+
+def _round_truncate(x, fmt):
+    x = np.asarray(x, np.float64)
+    if fmt == "f64":
+        return x.copy()
+    p, emin, emax = O.FORMATS[fmt]
+    out = x.copy()
+    m = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[m])
+    ue = np.maximum(e - p, emin - p + 1)
+    out[m] = np.ldexp(np.trunc(np.ldexp(x[m], -ue)), ue)
+    return out
+
+
+def _scores_sqrt_softplus_wrong(logits, scoring):
+    if scoring == "sqrt_softplus":
+        z = np.asarray(logits, np.float64)
+        return np.sqrt(np.log1p(np.exp(-np.abs(z))))   # dropped max(z, 0) term
+    return _orig_scores(logits, scoring)
+
+
+def _group_max_with_bias(s, top_k, correction_bias=None, num_expert_group=1, topk_group=1):
+    # group score = best biased score instead of the sum of the two best
+    if correction_bias is None:
+        return _orig_select(s, top_k, None, num_expert_group, topk_group)
+    s32 = O.round_to(s, "f32")
+    T, E = s32.shape
+    u = O.round_to(s32 + np.asarray(correction_bias)[None], "f32")
+    G, TG = num_expert_group, topk_group
+    sel = np.zeros((T, top_k), np.int64)
+    for t in range(T):
+        elig = np.ones(E, bool)
+        if G > 1:
+            gs = u[t].reshape(G, -1).max(1)
+            elig = np.isin(np.arange(E) // (E // G), O.ranked(gs)[:TG])
+        cand = np.nonzero(elig)[0]
+        sel[t] = cand[O.ranked(u[t, cand])][:top_k]
+    return sel, np.full(T, np.inf), np.full(T, np.inf)
+
+
+def _permute_unstable(topk_ids, num_experts):
+    off, srt, pos = _orig_permute(topk_ids, num_experts)
+    srt = srt.copy()
+    for e in range(num_experts):
+        srt[off[e]:off[e + 1]] = srt[off[e]:off[e + 1]][::-1]
+    pos = np.empty_like(srt)
+    pos[srt] = np.arange(srt.size)
+    return off, srt, pos
+
+
+def _ep_fill_everywhere_zero_scale(sel, wn, rsf, start, count, dtype):
+    rp, ws = _orig_ep(sel, wn, rsf, start, count, dtype)
+    return rp, np.where(ws == 0, O.round_to(rsf, dtype), ws)
+
+
+_orig_split = O.split_gate_up
+_orig_weights = O.routing_weights
+_orig_expert_mlp = O.expert_mlp
+_orig_scores = O.scores
+_orig_select = O.select_experts
+_orig_permute = O.permute
+_orig_ep = O.ep_router_outputs
+
+MUTANTS = {
+    "gate clamped from below too": ("swiglu", _swiglu_two_sided_gate),
+    "limit<=0 does not disable the clamp": ("swiglu", _swiglu_no_disable),
+    "gate and up halves swapped": ("split_gate_up", _split_swapped),
+    "ties go to the higher index": ("ranked", _ranked_high_index),
+    "scaling factor applied twice": ("routing_weights", _weights_rsf_twice),
+    "renormalized over all experts": ("routing_weights", _weights_biased),
+    "combine reads route_pos transposed": ("combine", _combine_transposed),
+    "down bias dropped": ("expert_mlp", _expert_mlp_no_down_bias),
+    "rounding truncates": ("round_to", _round_truncate),
+    "sqrt_softplus drops a term": ("scores", _scores_sqrt_softplus_wrong),
+    "biased group score is the max": ("select_experts", _group_max_with_bias),
+    "permute not stable": ("permute", _permute_unstable),
+    "no-local-expert scale not zero": ("ep_router_outputs", _ep_fill_everywhere_zero_scale),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(O, attr, fn)
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError, TypeError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake: {name}"
