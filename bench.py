@@ -1,0 +1,204 @@
+"""Benchmark of the routed MoE FFN forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one moe_ffn_forward over one batch: router, permute, grouped gate_up GEMM with
+the fused activation, grouped down GEMM and combine (and the shared expert when the
+workload has one). Inputs are seeded synthetic tensors already resident in HBM. W untimed
+steps, then K timed steps between two device synchronisations; rank 0 prints one JSON
+line. The dominant kernel (the grouped gate_up GEMM) is also timed on its own, launch by
+launch, with HIP events on the stream it runs on, for the roofline entry.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mixture_experts_ffn_moerouter_amd import binding as B  # noqa: E402
+from mixture_experts_ffn_moerouter_amd import inputs as I  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def distinct_experts(topk_ids: torch.Tensor) -> int:
+    return int(torch.unique(topk_ids).numel())
+
+
+def gate_up_algorithmic_bytes(cfg, n_experts: int) -> int:
+    """Bytes the gate_up kernel must move at minimum: each touched expert's [2F, H] weights
+    once, each token's hidden row once, each route's [F] activation row written once, and
+    the route index / offsets metadata."""
+    s = 4 if cfg.dtype == "f32" else 2
+    R = cfg.T * cfg.K
+    b = n_experts * 2 * cfg.F * cfg.H * s + cfg.T * cfg.H * s + R * cfg.F * s
+    if cfg.bias_std is not None:
+        b += n_experts * 2 * cfg.F * s
+    return b + R * 4 + (cfg.E + 1) * 4
+
+
+def layer_algorithmic(cfg, n_experts: int):
+    """Whole-layer minimum bytes and flops (weights of touched experts read once, inputs
+    read once, outputs written once, the activation written and read once)."""
+    s = 4 if cfg.dtype == "f32" else 2
+    R = cfg.T * cfg.K
+    by = n_experts * 3 * cfg.F * cfg.H * s + cfg.T * cfg.H * s + cfg.T * cfg.E * 4 \
+        + cfg.T * cfg.H * s + 2 * R * cfg.F * s
+    fl = 6 * R * cfg.H * cfg.F
+    if cfg.F_s:
+        by += 3 * cfg.F_s * cfg.H * s + cfg.T * cfg.H * s + 2 * cfg.T * cfg.F_s * s
+        fl += 6 * cfg.T * cfg.H * cfg.F_s
+    return by, fl
+
+
+def run_layer(cfg, d, fcfg, ws, out, shared_out):
+    B.moe_ffn_forward(fcfg, d["hidden"], d["logits"], d["w_gate_up"], d["w_down"],
+                      d.get("correction_bias"), d.get("expert_ids"), d.get("b_gate_up"),
+                      d.get("b_down"), d.get("shared_w_gate_up"), d.get("shared_w_down"),
+                      out=out, shared_out=shared_out, workspace=ws)
+
+
+def time_gate_up(cfg, d, reps: int):
+    """Average duration of one grouped gate_up GEMM launch, HIP events on its stream."""
+    stream = torch.cuda.current_stream()
+    w, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize,
+                                                        cfg.rsf, cfg.G, cfg.TG),
+                               d.get("correction_bias"), d.get("expert_ids"))
+    off, srt, pos, _ = B.moe_permute(ids, cfg.E)
+    act = torch.empty((cfg.T * cfg.K, cfg.F), dtype=cfg.torch_dtype, device="cuda")
+    call = lambda: B.moe_grouped_gemm_swiglu(d["hidden"], d["w_gate_up"], off, cfg.act,
+                                             d.get("b_gate_up"), a_rows=srt,
+                                             a_rows_div=cfg.K, out=act, stream=stream)
+    for _ in range(3):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)), distinct_experts(ids)
+
+
+def cpu_baseline(cfg, d, budget_s: float):
+    """The CPU oracle, as it stands, on the first n tokens of the same workload."""
+    import oracle.moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    host = {k: (v.float().cpu().numpy() if v.is_floating_point() else v.cpu().numpy())
+            for k, v in d.items()}
+    kw = dict(top_k=cfg.K, scoring=cfg.scoring, renormalize=cfg.renormalize,
+              routed_scaling_factor=cfg.rsf, num_expert_group=cfg.G, topk_group=cfg.TG,
+              act=cfg.act, dtype=cfg.dtype, correction_bias=host.get("correction_bias"),
+              expert_ids=host.get("expert_ids"), b_gate_up=host.get("b_gate_up"),
+              b_down=host.get("b_down"), shared_w_gate_up=host.get("shared_w_gate_up"),
+              shared_w_down=host.get("shared_w_down"))
+    n = min(cfg.T, 64)
+    while True:
+        t0 = time.perf_counter()
+        O.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
+                          host["w_down"], **kw)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 3 or n >= cfg.T:
+            break
+        n = min(cfg.T, n * 4)
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same workload, float64 numpy "
+                      f"oracle, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_bf16", choices=sorted(I.CONFIGS))
+    ap.add_argument("--backend", default="auto", choices=["auto", "staged", "indexed"])
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: the path is built and measured on a single "
+              "MI355X (no collectives); use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    cfg = I.CONFIGS[args.workload]
+    if cfg.H == 0:
+        sys.exit("router-only workload: not a bench line")
+    torch.cuda.set_device(0)
+    log(f"[bench] {cfg.name}: generating inputs")
+    d = I.make_inputs(cfg, device="cuda")
+    fcfg = B.ffn_cfg(cfg, args.backend)
+    backend = {1: "staged", 2: "indexed"}[B.moe_ffn_backend(fcfg, cfg.bias_std is not None)]
+    ws = torch.empty(B.moe_ffn_workspace_size(fcfg), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    shared_out = torch.empty_like(out) if cfg.F_s else None
+    log(f"[bench] backend {backend}; warmup {args.warmup}")
+    for _ in range(args.warmup):
+        run_layer(cfg, d, fcfg, ws, out, shared_out)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_layer(cfg, d, fcfg, ws, out, shared_out)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tokens_per_s = cfg.T * args.steps / elapsed
+
+    log("[bench] timing the gate_up kernel")
+    k_ms, n_exp = time_gate_up(cfg, d, args.kernel_reps)
+    k_bytes = gate_up_algorithmic_bytes(cfg, n_exp)
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    l_bytes, l_flops = layer_algorithmic(cfg, n_exp)
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs, random-init weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "F": cfg.F,
+                   "top_k": cfg.K, "scoring": cfg.scoring, "activation": cfg.act,
+                   "num_expert_group": cfg.G, "topk_group": cfg.TG, "F_shared": cfg.F_s,
+                   "backend": backend, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "gemm_bf16_kernel (grouped gate_up + SwiGLU)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes},
+        "layer": {"hbm_frac": round(l_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                  "mfma_frac": round(l_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                  "algorithmic_bytes": l_bytes, "flops": l_flops,
+                  "distinct_experts": n_exp},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,268 @@
+/*
+ * moe.h - C ABI of libmoe.so: the routed Mixture-of-Experts FFN forward on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, then section):
+ *   [MR]   ONNX Runtime pull request 32126, "[CUDA] Add MoERouter and SwiGLU contrib
+ *          operators".
+ *   [CPU]  onnx-light-cpu, "MoE (CPU)" kernel schema.
+ *   [SPEC] ONNX Runtime pull request 25619, "Update MoE and qMoE spec".
+ *   [TO]   TileOPs, "MoE Operators" API page.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers (HBM) unless said otherwise; every row is
+ *     contiguous ("row-major") and tensors are packed (no padding between rows).
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work:
+ *     they never synchronise the stream and never read device data on the host
+ *     ([TO] MoEGroupedGemmFwdOp: metadata is not checked, since checking would
+ *     synchronise). Device-side metadata (expert ids, offsets) outside its stated
+ *     range is a precondition violation, not an error that is reported.
+ *   - Ownership: the caller owns every buffer, including workspaces. The library
+ *     allocates no device memory and keeps no mutable global state; calls on one
+ *     stream are ordered, calls on different streams must not share output buffers.
+ *   - Errors: every argument check runs on the host before anything is enqueued; a
+ *     call that returns an error has launched nothing and written nothing. An output
+ *     that overlaps an input returns MOE_ERR_OVERLAP before any write ([TO]
+ *     MoEPostPermuteFwdOp, MoEGroupedGemmFwdOp: overlap is rejected before writing).
+ *   - Sizes of zero (T == 0, M == 0) return MOE_OK and launch nothing.
+ *   - dtypes: operands are MOE_F32 or MOE_BF16 (the same dtype for activations and
+ *     weights); router logits and routing weights are float32.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null required pointer, bad size or bad option      */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid per the pages, not implemented here           */
+  MOE_ERR_OVERLAP = 3,      /* an output overlaps an input                         */
+  MOE_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query returns */
+  MOE_ERR_LAUNCH = 5        /* the HIP runtime refused a launch                    */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_F16 = 2 } moe_dtype;
+
+/* [MR] MoERouter scoring attribute; [TO] FusedTopKFwdOp scoring_func. */
+typedef enum {
+  MOE_SCORE_SOFTMAX = 0,       /* softmax over all E logits                       */
+  MOE_SCORE_SIGMOID = 1,       /* 1 / (1 + exp(-z))                               */
+  MOE_SCORE_SQRT_SOFTPLUS = 2  /* sqrt(log(1 + exp(z)))                           */
+} moe_scoring;
+
+/* Row order of a [.., 2F, H] gate/up weight ([SPEC] Fusion Behavior; [TO]
+ * MoEGroupedGemmFwdOp): STACKED = F gate rows then F up rows; INTERLEAVED = row 2j is
+ * gate j and row 2j+1 is up j. */
+typedef enum { MOE_GU_STACKED = 0, MOE_GU_INTERLEAVED = 1 } moe_gu_layout;
+
+typedef enum { MOE_BACKEND_AUTO = 0, MOE_BACKEND_STAGED = 1, MOE_BACKEND_INDEXED = 2 }
+    moe_backend;
+
+/* Router options ([MR] MoERouter attributes; [TO] FusedTopKFwdOp __init__).
+ *   top_k                 experts per token, 1 <= top_k <= min(E, 32)
+ *   scoring               moe_scoring
+ *   renormalize           nonzero: divide the chosen scores by their sum
+ *   routed_scaling_factor > 0, multiplies the returned weights once, after the
+ *                         renormalization
+ *   num_expert_group      G >= 1 groups of E/G consecutive experts (E % G == 0, G <= 64)
+ *   topk_group            groups kept per token, 1 <= topk_group <= G, and the kept
+ *                         groups must hold at least top_k experts
+ *   local_expert_start/count  the expert-parallel slice [start, start+count) that
+ *                         router_probs describes (0 <= start, start+count <= E)
+ *   router_probs_dtype    moe_dtype of router_probs and weight_scale             */
+typedef struct {
+  int32_t top_k;
+  int32_t scoring;
+  int32_t renormalize;
+  float routed_scaling_factor;
+  int32_t num_expert_group;
+  int32_t topk_group;
+  int32_t local_expert_start;
+  int32_t local_expert_count;
+  int32_t router_probs_dtype;
+} moe_route_cfg;
+
+/* Gated activation of the gate_up GEMM ([MR] SwiGLU; [SPEC] SwiGLU Activation
+ * Function; [TO] MoEGroupedGemmFwdOp):
+ *   out_j = G * sigmoid(alpha * G) * (L + beta),  G = min(gate_j, limit),
+ *   L = clamp(up_j, -limit, limit); limit <= 0 turns both clamps off.
+ * silu_and_mul = {STACKED, 1, 0, 0}; swigluoai = {INTERLEAVED, 1.702, 1, 7}. */
+typedef struct {
+  int32_t layout; /* moe_gu_layout */
+  float alpha;
+  float beta;
+  float limit;
+} moe_act_cfg;
+
+/* Whole-layer configuration for moe_ffn_forward. F_shared = 0: no shared expert.
+ * dtype: operand dtype of hidden, weights, biases and outputs. backend: moe_backend. */
+typedef struct {
+  moe_route_cfg route;
+  moe_act_cfg act;
+  int64_t T, H, E, F, F_shared;
+  int32_t dtype;
+  int32_t backend;
+} moe_ffn_cfg;
+
+/* Text of a status code. Host only; never fails. */
+const char* moe_status_str(int status);
+
+/* Library ABI version (this header: 1). Host only. */
+int moe_abi_version(void);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route - router: scores, selection, weights, expert-parallel outputs.
+ * [MR] MoERouter; [TO] FusedTopKFwdOp and FusedMoEFwdOp (grouped routing).
+ *
+ * logits          [T, E] float32 router logits.
+ * correction_bias [E] float32 or NULL. Added to the scores for the selection only
+ *                 (noaux_tc); the weights use the unbiased scores.
+ * expert_ids      [T, top_k] int32 or NULL. When given, it replaces the selection
+ *                 (hash routing) and the bias and groups are ignored. Ids must lie in
+ *                 [0, E); repeated ids in a row are a precondition violation.
+ * Selection: the top_k experts with the largest float32 key (score + bias), ties to the
+ * lower expert index; with G > 1, only inside the topk_group groups whose score is
+ * largest (sum of the two best keys when a bias is given, else the best score; ties
+ * to the lower group). Each topk_ids row is ordered by key descending, ties by index.
+ * topk_weights    [T, top_k] float32 out: score of each chosen expert, divided by the
+ *                 sum of the chosen scores when renormalize, times
+ *                 routed_scaling_factor.
+ * topk_ids        [T, top_k] int32 out.
+ * router_probs    [T, local_expert_count] in router_probs_dtype, or NULL: log of the
+ *                 normalized weight (before routed_scaling_factor) at a chosen expert of
+ *                 the slice, -1e30 elsewhere (-1e4 for float16) [MR].
+ * weight_scale    [T] in router_probs_dtype, or NULL (given together with
+ *                 router_probs): routed_scaling_factor * sum of the normalized weights
+ *                 of the chosen experts in the slice; exactly 0 with none [MR].
+ * Errors: INVALID_ARG for null logits/topk outputs, E < 1, E > 512, bad cfg fields;
+ * OVERLAP if an output overlaps logits/bias/expert_ids or another output.
+ * ------------------------------------------------------------------------------- */
+int moe_route(const float* logits, int64_t T, int64_t E, const float* correction_bias,
+              const int32_t* expert_ids, const moe_route_cfg* cfg, float* topk_weights,
+              int32_t* topk_ids, void* router_probs, void* weight_scale, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_permute - expert-contiguous (tight, no padding) order of the R = T*top_k routes.
+ * [TO] MoEPrePermuteFwdOp, MoEPermuteAlignFwdOp (here without padding), and the
+ * contiguous layout of MoEGroupedGemmFwdOp.
+ *
+ * topk_ids        [T, K] int32 in [0, E); route r = t*K + k.
+ * expert_offsets  [E+1] int32 out: routes of expert e occupy permuted rows
+ *                 expert_offsets[e] .. expert_offsets[e+1]-1; expert_offsets[E] = R.
+ * sorted_route    [R] int32 out: the route at each permuted row; inside one expert the
+ *                 routes are in ascending r (a fixed order; the pages leave it open).
+ * route_pos       [R] int32 out: inverse of sorted_route (permuted row of route r).
+ * hidden, permuted  optional (both NULL or both given): permuted[m] =
+ *                 hidden[sorted_route[m] / K], rows of H elements of dtype dt.
+ * Limits: E <= 1024, R < 2^31. Errors: INVALID_ARG, OVERLAP.
+ * ------------------------------------------------------------------------------- */
+int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                int32_t* expert_offsets, int32_t* sorted_route, int32_t* route_pos,
+                const void* hidden, int64_t H, int32_t dt, void* permuted, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_grouped_gemm_swiglu - grouped gate_up GEMM with the gated activation in its
+ * epilogue; the [M, 2F] product is never written.
+ * [TO] MoEGroupedGemmFwdOp (activation fused, bias [E, 2F] in b's row order added to
+ * the float32 product before the activation), MoEExpertMLPFwdOp; [MR] SwiGLU.
+ *
+ * a               activations of dtype dt. If a_rows is NULL, a is [M, H] and row m of
+ *                 the product uses a[m]; otherwise row m uses a[a_rows[m] / a_rows_div]
+ *                 (a gather, e.g. hidden[T, H] with sorted_route and a_rows_div = K).
+ * w_gate_up       [E, 2F, H] dt, rows in act->layout order.
+ * b_gate_up       [E, 2F] dt or NULL.
+ * expert_offsets  [E+1] int32: rows of expert e are expert_offsets[e] ..
+ *                 expert_offsets[e+1]-1 (non-decreasing, expert_offsets[E] <= M).
+ * out             [M, F] dt: act(a W_e^T + b_e) rounded to dt (ties to even). Rows not
+ *                 covered by any expert are left unwritten.
+ * Accumulation is float32. Limits: H % 8 == 0 for bf16 (16-byte rows), E <= 1024.
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP (out vs a, weights, bias, offsets, a_rows).
+ * ------------------------------------------------------------------------------- */
+int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows_div,
+                            int64_t M, int64_t H, const void* w_gate_up,
+                            const void* b_gate_up, int64_t E, int64_t F,
+                            const int32_t* expert_offsets, int32_t dt,
+                            const moe_act_cfg* act, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_grouped_gemm - plain grouped GEMM: out[rows of e] = a[rows of e] b[e]^T + bias[e].
+ * [TO] MoEGroupedGemmFwdOp (contiguous layout, b is [E, N, K], float32 accumulation,
+ * output in the operand dtype unless float32 is asked for).
+ *
+ * a, a_rows, a_rows_div  as in moe_grouped_gemm_swiglu, with K columns.
+ * b               [E, N, K] dt.   bias  [E, N] dt or NULL.
+ * out             [M, N] in out_dt (dt or MOE_F32). Rows outside every expert are left
+ *                 unwritten.
+ * Limits: K % 8 == 0 for bf16, E <= 1024. Errors: INVALID_ARG, UNSUPPORTED, OVERLAP.
+ * ------------------------------------------------------------------------------- */
+int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, int64_t M,
+                     int64_t K, const void* b, const void* bias, int64_t E, int64_t N,
+                     const int32_t* expert_offsets, int32_t dt, int32_t out_dt, void* out,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine - back to token order, routing weights applied, top-k reduced, cast.
+ * [TO] MoEPostPermuteFwdOp (weights applied exactly once), FusedMoEExpertsFwdOp.
+ *
+ * y               [R, H] in y_dt (MOE_F32 or the operand dtype), permuted rows.
+ * topk_weights    [T, K] float32.   route_pos [T*K] int32 (from moe_permute).
+ * out             [T, H] out_dt: scale * sum_k topk_weights[t,k] * y[route_pos[t*K+k]],
+ *                 summed in float32 over k ascending, then rounded to out_dt.
+ * Errors: INVALID_ARG, OVERLAP (out vs y, topk_weights, route_pos).
+ * ------------------------------------------------------------------------------- */
+int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
+                const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
+                void* out, int32_t out_dt, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_ffn_workspace_size - bytes of device workspace moe_ffn_forward needs for cfg
+ * (for either backend). Host only; returns 0 for an invalid cfg.
+ * moe_ffn_backend - the backend moe_ffn_forward runs for cfg (MOE_BACKEND_STAGED or
+ * MOE_BACKEND_INDEXED), has_bias = whether b_gate_up or b_down is given. AUTO follows
+ * [TO] FusedMoEExpertsFwdOp: INDEXED when T*top_k <= 2E, the activation is
+ * silu_and_mul, there is no bias, H % 128 == 0 and F % 256 == 0; STAGED otherwise.
+ * Host only; returns -1 for an invalid cfg.
+ * ------------------------------------------------------------------------------- */
+size_t moe_ffn_workspace_size(const moe_ffn_cfg* cfg);
+int moe_ffn_backend(const moe_ffn_cfg* cfg, int has_bias);
+
+/* ---------------------------------------------------------------------------------
+ * moe_ffn_forward - the routed MoE FFN layer, plus the optional shared expert.
+ * [TO] FusedMoEFwdOp, FusedMoESharedExpertFwdOp, FusedMoEExpertsFwdOp,
+ * IndexedExpertMLPFwdOp, SharedExpertMLPFwdOp; [MR] MoERouter.
+ *
+ * hidden [T, H] dt; logits [T, E] float32; correction_bias [E] float32 or NULL;
+ * expert_ids [T, top_k] int32 or NULL (hash routing); w_gate_up [E, 2F, H] dt;
+ * w_down [E, H, F] dt; b_gate_up [E, 2F] dt or NULL; b_down [E, H] dt or NULL;
+ * shared_w_gate_up [2F_shared, H] dt (gate rows then up rows) and shared_w_down
+ * [H, F_shared] dt, required when cfg->F_shared > 0.
+ * out         [T, H] dt: sum_k w[t,k] (down_k(act(gate_up_k(h_t) + b_gu)) + b_down),
+ *             w including routed_scaling_factor (applied once).
+ * shared_out  [T, H] dt, or NULL when F_shared == 0: down(silu(h G^T) * (h U^T)),
+ *             the activation rounded to dt before the down projection; not scaled.
+ *             The caller adds out and shared_out when it needs the layer output.
+ * topk_weights_out [T, top_k] float32 / topk_ids_out [T, top_k] int32: optional
+ *             copies of the routing (NULL = not returned).
+ * workspace   device buffer of at least moe_ffn_workspace_size(cfg) bytes, 256-byte
+ *             aligned; its contents on entry do not matter.
+ * The router_probs outputs of cfg->route are not produced here (use moe_route).
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP, WORKSPACE.
+ * ------------------------------------------------------------------------------- */
+int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* logits,
+                    const float* correction_bias, const int32_t* expert_ids,
+                    const void* w_gate_up, const void* w_down, const void* b_gate_up,
+                    const void* b_down, const void* shared_w_gate_up,
+                    const void* shared_w_down, void* out, void* shared_out,
+                    float* topk_weights_out, int32_t* topk_ids_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

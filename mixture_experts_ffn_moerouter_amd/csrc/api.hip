@@ -1,0 +1,467 @@
+// Host side of libmoe.so: argument checks, overlap checks, workspace layout and the
+// launch order of each entry point declared in include/moe.h.
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using namespace moe;
+
+constexpr int kMaxRouteE = 512;   // the router keeps E/64 experts per lane, up to 8
+constexpr int kMaxGemmE = 1024;   // tile map and permute counters live in LDS
+constexpr int kMaxTopK = 32;
+
+size_t dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
+bool operand_dt_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool any_dt_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_F16; }
+
+// Byte ranges [p, p+n) overlap? Empty ranges and null pointers never overlap.
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + m && b < a + n;
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+// Does any output range overlap any input range, or another output?
+bool any_overlap(const Range* outs, int no, const Range* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i].p, outs[i].n, ins[j].p, ins[j].n)) return true;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i].p, outs[i].n, outs[j].p, outs[j].n)) return true;
+  }
+  return false;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+int check_route_cfg(const moe_route_cfg* c, int64_t E, bool need_slice) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->top_k < 1 || c->top_k > E || c->top_k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (c->scoring < 0 || c->scoring > 2) return MOE_ERR_INVALID_ARG;
+  if (!(c->routed_scaling_factor > 0.f)) return MOE_ERR_INVALID_ARG;
+  const int G = c->num_expert_group, TG = c->topk_group;
+  if (G < 1 || G > 64 || E % G != 0) return MOE_ERR_INVALID_ARG;
+  if (G > 1 && (TG < 1 || TG > G || (int64_t)TG * (E / G) < c->top_k))
+    return MOE_ERR_INVALID_ARG;
+  if (need_slice) {
+    if (!any_dt_ok(c->router_probs_dtype)) return MOE_ERR_INVALID_ARG;
+    if (c->local_expert_start < 0 || c->local_expert_count < 1 ||
+        (int64_t)c->local_expert_start + c->local_expert_count > E)
+      return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+bool act_ok(const moe_act_cfg* a) {
+  return a && (a->layout == MOE_GU_STACKED || a->layout == MOE_GU_INTERLEAVED);
+}
+
+bool is_silu_and_mul(const moe_act_cfg& a) {
+  return a.layout == MOE_GU_STACKED && a.alpha == 1.0f && a.beta == 0.0f && !(a.limit > 0.f);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace carve-up of moe_ffn_forward (both backends use the same layout).
+struct FfnWs {
+  size_t topk_w, topk_ids, offsets, sorted, pos, active, act, y, shared_act, total;
+};
+
+FfnWs ffn_ws_layout(const moe_ffn_cfg& c) {
+  FfnWs w;
+  const size_t R = (size_t)c.T * c.route.top_k, E = (size_t)c.E, s = dt_size(c.dtype);
+  size_t o = 0;
+  w.topk_w = o; o += align256(R * 4);
+  w.topk_ids = o; o += align256(R * 4);
+  w.offsets = o; o += align256((E + 1) * 4);
+  w.sorted = o; o += align256(R * 4);
+  w.pos = o; o += align256(R * 4);
+  w.active = o; o += align256((E + 1) * 4);
+  w.act = o; o += align256(R * (size_t)c.F * s);
+  const size_t y_elt = s > 4 ? s : 4;  // the indexed backend keeps y in float32
+  w.y = o; o += align256(R * (size_t)c.H * y_elt);
+  w.shared_act = o; o += align256((size_t)c.T * (size_t)c.F_shared * s);
+  w.total = o;
+  return w;
+}
+
+int check_ffn_cfg(const moe_ffn_cfg* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 0 || c->H < 1 || c->E < 1 || c->F < 1 || c->F_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (c->T * (int64_t)c->route.top_k >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!operand_dt_ok(c->dtype)) return MOE_ERR_UNSUPPORTED;
+  if (c->backend < MOE_BACKEND_AUTO || c->backend > MOE_BACKEND_INDEXED)
+    return MOE_ERR_INVALID_ARG;
+  int st = check_route_cfg(&c->route, c->E, false);
+  if (st) return st;
+  if (!act_ok(&c->act)) return MOE_ERR_INVALID_ARG;
+  if (c->E > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
+  if (c->dtype == MOE_BF16 && (c->H % 8 || c->F % 8 || c->F_shared % 8))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int backend_for(const moe_ffn_cfg& c, bool has_bias) {
+  const bool indexed_shape = c.dtype == MOE_BF16 && is_silu_and_mul(c.act) && !has_bias &&
+                             c.H % 128 == 0 && c.F % 256 == 0;
+  if (c.backend == MOE_BACKEND_STAGED) return MOE_BACKEND_STAGED;
+  if (c.backend == MOE_BACKEND_INDEXED) return indexed_shape ? MOE_BACKEND_INDEXED : -1;
+  return (c.T * c.route.top_k <= 2 * c.E && indexed_shape) ? MOE_BACKEND_INDEXED
+                                                         : MOE_BACKEND_STAGED;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape, dtype or option";
+    case MOE_ERR_OVERLAP: return "an output overlaps an input";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_abi_version(void) { return 1; }
+
+int moe_route(const float* logits, int64_t T, int64_t E, const float* correction_bias,
+              const int32_t* expert_ids, const moe_route_cfg* cfg, float* topk_weights,
+              int32_t* topk_ids, void* router_probs, void* weight_scale, void* stream) {
+  if (!logits || !topk_weights || !topk_ids || !cfg) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
+  if ((router_probs == nullptr) != (weight_scale == nullptr)) return MOE_ERR_INVALID_ARG;
+  int st = check_route_cfg(cfg, E, router_probs != nullptr);
+  if (st) return st;
+  if (T >= ((int64_t)1 << 31) / (E > cfg->top_k ? E : cfg->top_k)) return MOE_ERR_UNSUPPORTED;
+  const size_t K = cfg->top_k;
+  const size_t rps = router_probs ? dt_size(cfg->router_probs_dtype) : 0;
+  Range ins[] = {{logits, (size_t)T * E * 4}, {correction_bias, correction_bias ? (size_t)E * 4 : 0},
+                 {expert_ids, expert_ids ? (size_t)T * K * 4 : 0}};
+  Range outs[] = {{topk_weights, (size_t)T * K * 4}, {topk_ids, (size_t)T * K * 4},
+                  {router_probs, (size_t)T * (router_probs ? cfg->local_expert_count : 0) * rps},
+                  {weight_scale, (size_t)T * rps}};
+  if (any_overlap(outs, 4, ins, 3)) return MOE_ERR_OVERLAP;
+  if (T == 0) return MOE_OK;
+  RouteArgs a;
+  a.logits = logits;
+  a.bias = correction_bias;
+  a.expert_ids = expert_ids;
+  a.T = (int)T;
+  a.E = (int)E;
+  a.K = cfg->top_k;
+  a.scoring = cfg->scoring;
+  a.renormalize = cfg->renormalize != 0;
+  a.G = cfg->num_expert_group;
+  a.TG = cfg->topk_group;
+  a.rsf = cfg->routed_scaling_factor;
+  a.topk_w = topk_weights;
+  a.topk_ids = topk_ids;
+  a.router_probs = router_probs;
+  a.weight_scale = weight_scale;
+  a.rp_dtype = cfg->router_probs_dtype;
+  a.local_start = cfg->local_expert_start;
+  a.local_count = cfg->local_expert_count;
+  return status_of(launch_route(a, (hipStream_t)stream));
+}
+
+int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                int32_t* expert_offsets, int32_t* sorted_route, int32_t* route_pos,
+                const void* hidden, int64_t H, int32_t dt, void* permuted, void* stream) {
+  if (!topk_ids || !expert_offsets || !sorted_route || !route_pos) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if ((hidden == nullptr) != (permuted == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (hidden && (H < 1 || !operand_dt_ok(dt))) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
+  if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const size_t R = (size_t)(T * K);
+  const size_t row = hidden ? (size_t)H * dt_size(dt) : 0;
+  Range ins[] = {{topk_ids, R * 4}, {hidden, (size_t)T * row}};
+  Range outs[] = {{expert_offsets, (size_t)(E + 1) * 4}, {sorted_route, R * 4},
+                  {route_pos, R * 4}, {permuted, R * row}};
+  if (any_overlap(outs, 4, ins, 2)) return MOE_ERR_OVERLAP;
+  hipStream_t s = (hipStream_t)stream;
+  int st = status_of(launch_permute(topk_ids, (int)R, (int)E, expert_offsets, sorted_route,
+                                    route_pos, nullptr, s));
+  if (st || !hidden || R == 0) return st;
+  return status_of(launch_gather_rows(hidden, sorted_route, (int)K, (int)R, (int64_t)row,
+                                      permuted, s));
+}
+
+static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_rows_div,
+                               int64_t M, int64_t Kd, const void* b, const void* bias,
+                               int64_t E, int64_t Nw, bool act_on, const moe_act_cfg* act,
+                               const int32_t* offsets, int32_t dt, int32_t out_dt, void* out,
+                               void* stream) {
+  if (!a || !b || !offsets || !out) return MOE_ERR_INVALID_ARG;
+  if (M < 0 || Kd < 1 || E < 1 || Nw < 1) return MOE_ERR_INVALID_ARG;
+  if (a_rows && a_rows_div < 1) return MOE_ERR_INVALID_ARG;
+  if (act_on && !act_ok(act)) return MOE_ERR_INVALID_ARG;
+  if (!operand_dt_ok(dt) || !(out_dt == dt || out_dt == MOE_F32)) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
+  if (M >= ((int64_t)1 << 31) || Nw >= ((int64_t)1 << 30) || Kd >= ((int64_t)1 << 30))
+    return MOE_ERR_UNSUPPORTED;
+  if (dt == MOE_BF16 && Kd % 8) return MOE_ERR_UNSUPPORTED;
+  if (dt == MOE_F32 && Kd > 12288) return MOE_ERR_UNSUPPORTED;  // A row staged in LDS
+  const int64_t Nout = act_on ? Nw / 2 : Nw;
+  const size_t s = dt_size(dt);
+  Range ins[] = {{b, (size_t)E * Nw * Kd * s}, {bias, bias ? (size_t)E * Nw * s : 0},
+                 {offsets, (size_t)(E + 1) * 4}, {a_rows, a_rows ? (size_t)M * 4 : 0},
+                 {a, a_rows ? 1 : (size_t)M * Kd * s}};
+  Range outs[] = {{out, (size_t)M * Nout * dt_size(out_dt)}};
+  if (any_overlap(outs, 1, ins, 5)) return MOE_ERR_OVERLAP;
+  if (M == 0) return MOE_OK;
+  GemmArgs g;
+  g.a = a;
+  g.a_rows = a_rows;
+  g.a_rows_div = a_rows_div < 1 ? 1 : a_rows_div;
+  g.M = (int)M;
+  g.Kd = (int)Kd;
+  g.b = b;
+  g.bias = bias;
+  g.offsets = offsets;
+  g.E = (int)E;
+  g.Nw = (int)Nw;
+  g.act = act_on;
+  g.layout = act_on ? act->layout : 0;
+  g.alpha = act_on ? act->alpha : 1.f;
+  g.beta = act_on ? act->beta : 0.f;
+  g.limit = act_on ? act->limit : 0.f;
+  g.out = out;
+  g.Nout = (int)Nout;
+  g.dt = dt;
+  g.out_dt = out_dt;
+  return status_of(launch_grouped_gemm(g, (hipStream_t)stream));
+}
+
+int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows_div,
+                            int64_t M, int64_t H, const void* w_gate_up,
+                            const void* b_gate_up, int64_t E, int64_t F,
+                            const int32_t* expert_offsets, int32_t dt,
+                            const moe_act_cfg* act, void* out, void* stream) {
+  if (F < 1) return MOE_ERR_INVALID_ARG;
+  return grouped_gemm_common(a, a_rows, a_rows_div, M, H, w_gate_up, b_gate_up, E, 2 * F,
+                             true, act, expert_offsets, dt, dt, out, stream);
+}
+
+int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, int64_t M,
+                     int64_t K, const void* b, const void* bias, int64_t E, int64_t N,
+                     const int32_t* expert_offsets, int32_t dt, int32_t out_dt, void* out,
+                     void* stream) {
+  return grouped_gemm_common(a, a_rows, a_rows_div, M, K, b, bias, E, N, false, nullptr,
+                             expert_offsets, dt, out_dt, out, stream);
+}
+
+int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
+                const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
+                void* out, int32_t out_dt, void* stream) {
+  if (!y || !topk_weights || !route_pos || !out) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (!operand_dt_ok(y_dt) || !any_dt_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
+  if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const size_t R = (size_t)(T * K);
+  Range ins[] = {{y, R * H * dt_size(y_dt)}, {topk_weights, R * 4}, {route_pos, R * 4}};
+  Range outs[] = {{out, (size_t)T * H * dt_size(out_dt)}};
+  if (any_overlap(outs, 1, ins, 3)) return MOE_ERR_OVERLAP;
+  if (T == 0) return MOE_OK;
+  return status_of(launch_combine(y, y_dt, topk_weights, route_pos, (int)T, (int)K, (int)H,
+                                  scale, out, out_dt, (hipStream_t)stream));
+}
+
+size_t moe_ffn_workspace_size(const moe_ffn_cfg* cfg) {
+  if (check_ffn_cfg(cfg) != MOE_OK) return 0;
+  return ffn_ws_layout(*cfg).total;
+}
+
+int moe_ffn_backend(const moe_ffn_cfg* cfg, int has_bias) {
+  if (check_ffn_cfg(cfg) != MOE_OK) return -1;
+  return backend_for(*cfg, has_bias != 0);
+}
+
+int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* logits,
+                    const float* correction_bias, const int32_t* expert_ids,
+                    const void* w_gate_up, const void* w_down, const void* b_gate_up,
+                    const void* b_down, const void* shared_w_gate_up,
+                    const void* shared_w_down, void* out, void* shared_out,
+                    float* topk_weights_out, int32_t* topk_ids_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_ffn_cfg(cfg);
+  if (st) return st;
+  const moe_ffn_cfg& c = *cfg;
+  if (!hidden || !logits || !w_gate_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
+  if (c.F_shared > 0 && (!shared_w_gate_up || !shared_w_down || !shared_out))
+    return MOE_ERR_INVALID_ARG;
+  if (c.F_shared == 0 && shared_out) return MOE_ERR_INVALID_ARG;
+  const int backend = backend_for(c, b_gate_up || b_down);
+  if (backend < 0) return MOE_ERR_UNSUPPORTED;
+  const FfnWs w = ffn_ws_layout(c);
+  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255))
+    return MOE_ERR_WORKSPACE;
+
+  const size_t s = dt_size(c.dtype), T = (size_t)c.T, H = (size_t)c.H, E = (size_t)c.E,
+               F = (size_t)c.F, K = (size_t)c.route.top_k, Fs = (size_t)c.F_shared;
+  Range ins[] = {{hidden, T * H * s},
+                 {logits, T * E * 4},
+                 {correction_bias, correction_bias ? E * 4 : 0},
+                 {expert_ids, expert_ids ? T * K * 4 : 0},
+                 {w_gate_up, E * 2 * F * H * s},
+                 {w_down, E * H * F * s},
+                 {b_gate_up, b_gate_up ? E * 2 * F * s : 0},
+                 {b_down, b_down ? E * H * s : 0},
+                 {shared_w_gate_up, shared_w_gate_up ? 2 * Fs * H * s : 0},
+                 {shared_w_down, shared_w_down ? H * Fs * s : 0},
+                 {workspace, w.total}};
+  Range outs[] = {{out, T * H * s},
+                  {shared_out, shared_out ? T * H * s : 0},
+                  {topk_weights_out, topk_weights_out ? T * K * 4 : 0},
+                  {topk_ids_out, topk_ids_out ? T * K * 4 : 0}};
+  if (any_overlap(outs, 4, ins, 11)) return MOE_ERR_OVERLAP;
+  if (c.T == 0) return MOE_OK;
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* topk_w = topk_weights_out ? topk_weights_out : (float*)(ws + w.topk_w);
+  int32_t* topk_ids = topk_ids_out ? topk_ids_out : (int32_t*)(ws + w.topk_ids);
+  int32_t* offsets = (int32_t*)(ws + w.offsets);
+  int32_t* sorted = (int32_t*)(ws + w.sorted);
+  int32_t* pos = (int32_t*)(ws + w.pos);
+  int32_t* active = (int32_t*)(ws + w.active);
+  void* act = ws + w.act;
+  void* y = ws + w.y;
+  const int R = (int)(T * K);
+
+  // 1. router
+  RouteArgs ra;
+  ra.logits = logits;
+  ra.bias = correction_bias;
+  ra.expert_ids = expert_ids;
+  ra.T = (int)T;
+  ra.E = (int)E;
+  ra.K = (int)K;
+  ra.scoring = c.route.scoring;
+  ra.renormalize = c.route.renormalize != 0;
+  ra.G = c.route.num_expert_group;
+  ra.TG = c.route.topk_group;
+  ra.rsf = c.route.routed_scaling_factor;
+  ra.topk_w = topk_w;
+  ra.topk_ids = topk_ids;
+  ra.router_probs = nullptr;
+  ra.weight_scale = nullptr;
+  ra.rp_dtype = 0;
+  ra.local_start = 0;
+  ra.local_count = 0;
+  if ((st = status_of(launch_route(ra, strm)))) return st;
+  // 2. permute (expert-contiguous order; active-expert list for the indexed backend)
+  if ((st = status_of(launch_permute(topk_ids, R, (int)E, offsets, sorted, pos,
+                                     backend == MOE_BACKEND_INDEXED ? active : nullptr,
+                                     strm))))
+    return st;
+  int y_dt = c.dtype;
+  if (backend == MOE_BACKEND_INDEXED) {
+    IndexedArgs ia;
+    ia.hidden = (const uint16_t*)hidden;
+    ia.sorted_route = sorted;
+    ia.offsets = offsets;
+    ia.active = active;
+    ia.w_gate_up = (const uint16_t*)w_gate_up;
+    ia.w_down = (const uint16_t*)w_down;
+    ia.T = (int)T;
+    ia.H = (int)H;
+    ia.E = (int)E;
+    ia.F = (int)F;
+    ia.K = (int)K;
+    ia.act = (uint16_t*)act;
+    ia.y = (float*)y;
+    if ((st = status_of(launch_indexed_mlp(ia, strm)))) return st;
+    y_dt = MOE_F32;
+  } else {
+    // 3. gate_up GEMM + activation, A rows gathered from hidden by route
+    GemmArgs g;
+    g.a = hidden;
+    g.a_rows = sorted;
+    g.a_rows_div = (int)K;
+    g.M = R;
+    g.Kd = (int)H;
+    g.b = w_gate_up;
+    g.bias = b_gate_up;
+    g.offsets = offsets;
+    g.E = (int)E;
+    g.Nw = (int)(2 * F);
+    g.act = 1;
+    g.layout = c.act.layout;
+    g.alpha = c.act.alpha;
+    g.beta = c.act.beta;
+    g.limit = c.act.limit;
+    g.out = act;
+    g.Nout = (int)F;
+    g.dt = c.dtype;
+    g.out_dt = c.dtype;
+    if ((st = status_of(launch_grouped_gemm(g, strm)))) return st;
+    // 4. down GEMM (+ b_down), expert output stored in the operand dtype
+    GemmArgs d = g;
+    d.a = act;
+    d.a_rows = nullptr;
+    d.a_rows_div = 1;
+    d.Kd = (int)F;
+    d.b = w_down;
+    d.bias = b_down;
+    d.Nw = (int)H;
+    d.act = 0;
+    d.out = y;
+    d.Nout = (int)H;
+    if ((st = status_of(launch_grouped_gemm(d, strm)))) return st;
+  }
+  // 5. weighted combine (routed_scaling_factor is already in the weights)
+  if ((st = status_of(launch_combine(y, y_dt, topk_w, pos, (int)T, (int)K, (int)H, 1.0f, out,
+                                     c.dtype, strm))))
+    return st;
+  // 6. shared expert: one "expert" owning every token
+  if (c.F_shared > 0) {
+    GemmArgs g;
+    g.a = hidden;
+    g.a_rows = nullptr;
+    g.a_rows_div = 1;
+    g.M = (int)T;
+    g.Kd = (int)H;
+    g.b = shared_w_gate_up;
+    g.bias = nullptr;
+    g.offsets = nullptr;
+    g.E = 1;
+    g.Nw = (int)(2 * Fs);
+    g.act = 1;
+    g.layout = MOE_GU_STACKED;
+    g.alpha = 1.f;
+    g.beta = 0.f;
+    g.limit = 0.f;
+    g.out = ws + w.shared_act;
+    g.Nout = (int)Fs;
+    g.dt = c.dtype;
+    g.out_dt = c.dtype;
+    if ((st = status_of(launch_grouped_gemm(g, strm)))) return st;
+    GemmArgs d = g;
+    d.a = ws + w.shared_act;
+    d.Kd = (int)Fs;
+    d.b = shared_w_down;
+    d.Nw = (int)H;
+    d.act = 0;
+    d.out = shared_out;
+    d.Nout = (int)H;
+    if ((st = status_of(launch_grouped_gemm(d, strm)))) return st;
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

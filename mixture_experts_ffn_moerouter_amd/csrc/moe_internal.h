@@ -1,0 +1,99 @@
+// Internal declarations shared by the HIP translation units of libmoe.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ------------------------------------------------------------------ device helpers
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// bfloat16 <-> float32. The narrowing rounds to nearest, ties to even (the usual
+// add-0x7fff-plus-lsb method); NaNs stay NaN.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+// Store one float32 value in dtype `dt` (0 f32, 1 bf16, 2 f16) at element i of p.
+__device__ __forceinline__ void store_dt(void* p, int dt, int64_t i, float v) {
+  if (dt == 0) ((float*)p)[i] = v;
+  else if (dt == 1) ((uint16_t*)p)[i] = f32_to_bf16(v);
+  else ((uint16_t*)p)[i] = f32_to_f16(v);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// ------------------------------------------------------------------ launchers
+// Each returns a hipError_t; arguments are validated by the caller (api.hip).
+struct RouteArgs {
+  const float* logits;
+  const float* bias;
+  const int32_t* expert_ids;
+  int T, E, K, scoring, renormalize, G, TG;
+  float rsf;
+  float* topk_w;
+  int32_t* topk_ids;
+  void* router_probs;
+  void* weight_scale;
+  int rp_dtype, local_start, local_count;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// active_list: optional [E+1] int32 out; active_list[0..n) = experts with routes, in
+// ascending order, and active_list[E] = n.
+hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets,
+                          int32_t* sorted_route, int32_t* route_pos, int32_t* active_list,
+                          hipStream_t s);
+hipError_t launch_gather_rows(const void* src, const int32_t* rows, int div, int M,
+                              int64_t row_bytes, void* dst, hipStream_t s);
+
+struct GemmArgs {
+  const void* a;
+  const int32_t* a_rows;
+  int a_rows_div;
+  int M, Kd;          // logical rows, contraction length
+  const void* b;      // [E, Nw, Kd]
+  const void* bias;   // [E, Nw] or null
+  const int32_t* offsets;
+  int E, Nw;          // weight rows per expert
+  int act;            // 0 none, 1 gated activation
+  int layout;         // moe_gu_layout when act
+  float alpha, beta, limit;
+  void* out;          // [M, Nout]
+  int Nout;           // Nw or Nw/2
+  int dt, out_dt;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
+
+hipError_t launch_combine(const void* y, int y_dt, const float* w, const int32_t* route_pos,
+                          int T, int K, int H, float scale, void* out, int out_dt,
+                          hipStream_t s);
+
+// Indexed small-route backend (bf16, silu_and_mul, no bias).
+struct IndexedArgs {
+  const uint16_t* hidden;     // [T, H]
+  const int32_t* sorted_route;
+  const int32_t* offsets;     // [E+1]
+  const int32_t* active;      // [E+1] from launch_permute
+  const uint16_t* w_gate_up;  // [E, 2F, H] stacked
+  const uint16_t* w_down;     // [E, H, F]
+  int T, H, E, F, K;
+  uint16_t* act;              // [R, F] workspace (permuted rows)
+  float* y;                   // [R, H] workspace (permuted rows)
+};
+hipError_t launch_indexed_mlp(const IndexedArgs& a, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,240 @@
+// Router kernel: scoring, (grouped) top-k selection, weights and the expert-parallel
+// router row, one wave64 per token.
+//
+// [MR] ONNX Runtime PR 32126 "[CUDA] Add MoERouter and SwiGLU contrib operators",
+//      MoERouter: scoring softmax | sigmoid | sqrt_softplus, selection topk | noaux_tc
+//      (bias added before the top-k), ties to the lower expert index, expert_ids hash
+//      override, router_probs / weight_scale for a local expert slice.
+// [TO] TileOPs "MoE Operators", FusedTopKFwdOp / FusedMoEFwdOp: float32 scoring and
+//      selection, DeepSeek-V3 group limit, renormalize, routed_scaling_factor once.
+//
+// Layout: lane l of the token's wave holds experts l, l+64, l+128, ... (coalesced
+// loads of the logits row). A selection key is the 64-bit integer
+// (order-preserving bits of the float32 key) << 32 | (0xffffffff - expert), so the
+// largest key is the largest value and, among equal values, the lowest index; one
+// wave-wide max per round picks the next expert.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ uint32_t order_bits(float x) {
+  if (x == 0.0f) x = 0.0f;  // -0.0 and +0.0 compare equal, so give them one key
+  uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t make_key(float v, int idx) {
+  return ((uint64_t)order_bits(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ int key_index(uint64_t k) {
+  return (int)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
+  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// Top two values of a wave (a1 >= a2 in every lane on entry and exit).
+__device__ __forceinline__ void wave_top2(float& a1, float& a2) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    float b1 = __shfl_xor(a1, m, 64), b2 = __shfl_xor(a2, m, 64);
+    float n1 = fmaxf(a1, b1);
+    float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+    a1 = n1;
+    a2 = n2;
+  }
+}
+
+template <int PL>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (t >= p.T) return;  // uniform per wave
+  const int E = p.E;
+  const float* z = p.logits + (int64_t)t * E;
+
+  float s[PL], u[PL];
+  bool valid[PL];
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    int e = lane + 64 * j;
+    valid[j] = e < E;
+    s[j] = valid[j] ? z[e] : -INFINITY;
+  }
+  // ---- scoring, float32
+  if (p.scoring == 0) {  // softmax over all E experts
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) m = fmaxf(m, s[j]);
+    m = wave_max_f32(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < PL; ++j) {
+      s[j] = valid[j] ? expf(s[j] - m) : 0.f;
+      sum += s[j];
+    }
+    sum = wave_sum_f32(sum);
+#pragma unroll
+    for (int j = 0; j < PL; ++j) s[j] = s[j] / sum;
+  } else if (p.scoring == 1) {  // sigmoid
+#pragma unroll
+    for (int j = 0; j < PL; ++j) s[j] = valid[j] ? 1.0f / (1.0f + expf(-s[j])) : 0.f;
+  } else {  // sqrt(softplus(z)) = sqrt(max(z,0) + log1p(exp(-|z|)))
+#pragma unroll
+    for (int j = 0; j < PL; ++j)
+      s[j] = valid[j] ? sqrtf(fmaxf(s[j], 0.f) + log1pf(expf(-fabsf(s[j])))) : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PL; ++j) {
+    int e = lane + 64 * j;
+    u[j] = (p.bias && valid[j]) ? s[j] + p.bias[e] : s[j];
+  }
+
+  // Lane k (< K) ends up holding the k-th chosen expert and its unbiased score.
+  int my_sel = 0;
+  float my_w = 0.f;
+  float wsum = 0.f;  // sum of the chosen scores, k ascending (uniform)
+  const int K = p.K;
+
+  if (p.expert_ids) {
+    // ---- hash routing: the given experts, bias and groups ignored
+    for (int k = 0; k < K; ++k) {
+      int e = p.expert_ids[(int64_t)t * K + k];
+      int slot = e >> 6;
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < PL; ++j)
+        if (j == slot) v = s[j];
+      float w = __shfl(v, e & 63, 64);
+      wsum += w;
+      if (lane == k) { my_sel = e; my_w = w; }
+    }
+  } else {
+    bool elig[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) elig[j] = valid[j];
+    if (p.G > 1) {
+      // ---- group limit: lane g computes the score of group g
+      const int gsz = E / p.G;
+      float my_gs = -INFINITY;
+      for (int g = 0; g < p.G; ++g) {
+        float a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < PL; ++j) {
+          int e = lane + 64 * j;
+          if (valid[j] && e / gsz == g) {
+            float v = u[j];
+            if (v > a1) { a2 = a1; a1 = v; }
+            else if (v > a2) { a2 = v; }
+          }
+        }
+        wave_top2(a1, a2);
+        float gs = (p.bias && gsz >= 2) ? a1 + a2 : a1;
+        if (lane == g) my_gs = gs;
+      }
+      uint64_t gkey = lane < p.G ? make_key(my_gs, lane) : 0ull;
+      uint64_t kept = 0ull;
+      for (int i = 0; i < p.TG; ++i) {
+        uint64_t m = wave_max_u64(gkey);
+        int g = key_index(m);
+        kept |= 1ull << g;
+        if (lane == g) gkey = 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < PL; ++j) {
+        int e = lane + 64 * j;
+        if (valid[j]) elig[j] = (kept >> (e / gsz)) & 1ull;
+      }
+    }
+    // ---- top-k: K rounds of a wave-wide max over the remaining eligible keys
+    uint64_t keys[PL];
+#pragma unroll
+    for (int j = 0; j < PL; ++j) keys[j] = elig[j] ? make_key(u[j], lane + 64 * j) : 0ull;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = 0ull;
+      float best_s = 0.f;
+#pragma unroll
+      for (int j = 0; j < PL; ++j)
+        if (keys[j] > best) { best = keys[j]; best_s = s[j]; }
+      uint64_t m = wave_max_u64(best);
+      int e = key_index(m);
+      float w = __shfl(best_s, e & 63, 64);
+#pragma unroll
+      for (int j = 0; j < PL; ++j)
+        if (lane + 64 * j == e) keys[j] = 0ull;
+      wsum += w;
+      if (lane == k) { my_sel = e; my_w = w; }
+    }
+  }
+
+  // ---- weights: renormalize, then routed_scaling_factor once
+  float wn = p.renormalize ? my_w / wsum : my_w;
+  if (lane < K) {
+    p.topk_w[(int64_t)t * K + lane] = wn * p.rsf;
+    p.topk_ids[(int64_t)t * K + lane] = my_sel;
+  }
+
+  // ---- expert-parallel router row and scale
+  if (p.router_probs) {
+    const int a0 = p.local_start, n = p.local_count;
+    const float fill = p.rp_dtype == 2 ? -1.0e4f : -1.0e30f;
+    float w_local = 0.f;  // k ascending, uniform
+    for (int k = 0; k < K; ++k) {
+      int e = __shfl(my_sel, k, 64);
+      float w = __shfl(wn, k, 64);
+      if (e >= a0 && e < a0 + n) w_local += w;
+    }
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      int c = c0 + lane;
+      float v = fill;
+      for (int k = 0; k < K; ++k) {
+        int e = __shfl(my_sel, k, 64);
+        float w = __shfl(wn, k, 64);
+        if (e == a0 + c) v = logf(w);
+      }
+      if (c < n) store_dt(p.router_probs, p.rp_dtype, (int64_t)t * n + c, v);
+    }
+    if (lane == 0) store_dt(p.weight_scale, p.rp_dtype, t, p.rsf * w_local);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  dim3 grid((a.T + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
+  if (a.E <= 64) route_kernel<1><<<grid, block, 0, s>>>(a);
+  else if (a.E <= 128) route_kernel<2><<<grid, block, 0, s>>>(a);
+  else if (a.E <= 256) route_kernel<4><<<grid, block, 0, s>>>(a);
+  else route_kernel<8><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,156 @@
+"""The C ABI on the host: the library loads, exports every symbol include/moe.h declares,
+and its host-only logic (status text, workspace sizing, backend choice, argument and
+overlap checks that return before any launch) behaves as the header states.
+No call here reaches the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle.moe_oracle as O
+from mixture_experts_ffn_moerouter_amd import binding as B
+from mixture_experts_ffn_moerouter_amd import inputs as I
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) == 10, names
+    assert set(names) == set(B.SYMBOLS)
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    L = B.lib()
+    assert L.moe_abi_version() == 1
+    texts = {L.moe_status_str(s).decode() for s in range(6)}
+    assert len(texts) == 6
+    assert L.moe_status_str(99).decode() == "unknown status"
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(B.MoeRouteCfg) == 36
+    assert ctypes.sizeof(B.MoeActCfg) == 16
+    assert ctypes.sizeof(B.MoeFfnCfg) == 104
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_bf16", "gptoss_bf16", "dsv3_bf16",
+                                  "decode_dsv3_bf16"])
+def test_backend_choice_follows_dispatch_rule(name):
+    cfg = I.CONFIGS[name]
+    has_bias = cfg.bias_std is not None
+    want_indexed = O.indexed_backend_applies(cfg.T, cfg.K, cfg.E, cfg.H, cfg.F, cfg.act,
+                                             has_bias) and cfg.dtype == "bf16"
+    got = B.moe_ffn_backend(B.ffn_cfg(cfg), has_bias)
+    assert got == (2 if want_indexed else 1)
+    assert B.moe_ffn_backend(B.ffn_cfg(cfg, "staged"), has_bias) == 1
+    forced = B.moe_ffn_backend(B.ffn_cfg(cfg, "indexed"), has_bias)
+    assert forced == (2 if (cfg.dtype == "bf16" and not has_bias and cfg.act == "silu_and_mul"
+                            and cfg.H % 128 == 0 and cfg.F % 256 == 0) else -1)
+
+
+def test_workspace_size_covers_buffers():
+    cfg = I.CONFIGS["dsv3_bf16"]
+    ws = B.moe_ffn_workspace_size(B.ffn_cfg(cfg))
+    R = cfg.T * cfg.K
+    assert ws >= R * cfg.F * 2 + R * cfg.H * 4 + cfg.T * cfg.F_s * 2
+    assert ws % 256 == 0
+    bad = B.ffn_cfg(cfg.with_(E=250))     # E % G != 0
+    assert B.moe_ffn_workspace_size(bad) == 0
+    assert B.moe_ffn_backend(bad, False) == -1
+
+
+FAKE = 0x7f0000000000  # never dereferenced: every call below fails its host checks
+
+
+def _route(T=4, E=8, cfg=None, logits=FAKE, bias=None, ids=None, w=FAKE + 4096,
+           tids=FAKE + 8192, rp=None, ws=None):
+    cfg = cfg or B.route_cfg(2)
+    return B.lib().moe_route(logits, T, E, bias, ids, ctypes.byref(cfg), w, tids, rp, ws, None)
+
+
+def test_route_argument_errors():
+    assert _route(logits=None) == B.MOE_ERR_INVALID_ARG
+    assert _route(E=0) == B.MOE_ERR_INVALID_ARG
+    assert _route(E=600) == B.MOE_ERR_UNSUPPORTED
+    assert _route(cfg=B.route_cfg(9)) == B.MOE_ERR_INVALID_ARG            # K > E
+    assert _route(cfg=B.route_cfg(2, routed_scaling_factor=0.0)) == B.MOE_ERR_INVALID_ARG
+    assert _route(cfg=B.route_cfg(2, num_expert_group=3)) == B.MOE_ERR_INVALID_ARG  # 8 % 3
+    assert _route(cfg=B.route_cfg(2, num_expert_group=4, topk_group=5)) == \
+        B.MOE_ERR_INVALID_ARG
+    assert _route(cfg=B.route_cfg(3, num_expert_group=4, topk_group=1)) == \
+        B.MOE_ERR_INVALID_ARG                                             # 1 group < K
+    assert _route(rp=FAKE + 65536) == B.MOE_ERR_INVALID_ARG               # scale missing
+    assert _route(rp=FAKE + 65536, ws=FAKE + 131072,
+                  cfg=B.route_cfg(2, local_expert_start=6, local_expert_count=4)) == \
+        B.MOE_ERR_INVALID_ARG                                             # slice past E
+    # outputs overlapping the logits, or each other
+    assert _route(w=FAKE + 8) == B.MOE_ERR_OVERLAP
+    assert _route(tids=FAKE + 4096 + 16) == B.MOE_ERR_OVERLAP
+
+
+def test_gemm_combine_permute_argument_errors():
+    L = B.lib()
+    act = B.act_cfg("silu_and_mul")
+    # out overlapping the weights
+    st = L.moe_grouped_gemm_swiglu(FAKE, None, 1, 16, 64, FAKE + (1 << 20), None, 2, 32,
+                                   FAKE + (1 << 24), 1, ctypes.byref(act), FAKE + (1 << 20) + 64,
+                                   None)
+    assert st == B.MOE_ERR_OVERLAP
+    # bf16 rows must be a multiple of 8 elements
+    st = L.moe_grouped_gemm(FAKE, None, 1, 16, 60, FAKE + (1 << 20), None, 2, 32,
+                            FAKE + (1 << 24), 1, 1, FAKE + (1 << 28), None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    # out dtype must be the operand dtype or f32
+    st = L.moe_grouped_gemm(FAKE, None, 1, 16, 64, FAKE + (1 << 20), None, 2, 32,
+                            FAKE + (1 << 24), 1, 2, FAKE + (1 << 28), None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    st = L.moe_grouped_gemm(None, None, 1, 16, 64, FAKE, None, 2, 32, FAKE, 1, 1, FAKE, None)
+    assert st == B.MOE_ERR_INVALID_ARG
+    st = L.moe_combine(FAKE, 1, FAKE + (1 << 20), FAKE + (1 << 21), 4, 2, 64, 1.0, FAKE + 32,
+                       1, None)
+    assert st == B.MOE_ERR_OVERLAP
+    st = L.moe_permute(FAKE, 4, 2, 2000, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, 0, 0,
+                       None, None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    st = L.moe_permute(FAKE, 4, 2, 8, FAKE + 4, FAKE + 8192, FAKE + 12288, None, 0, 0, None,
+                       None)
+    assert st == B.MOE_ERR_OVERLAP
+
+
+def test_ffn_argument_errors():
+    L = B.lib()
+    cfg = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
+    args = [FAKE + i * (1 << 24) for i in range(14)]
+    ffn = lambda c, a, ws=FAKE + (1 << 40), n=1 << 30: L.moe_ffn_forward(
+        ctypes.byref(c), *a, ws, n, None)
+    # hidden, logits, bias, expert_ids, w_gate_up, w_down, b_gate_up, b_down,
+    # shared_w_gate_up, shared_w_down, out, shared_out, topk_weights_out, topk_ids_out
+    a = list(args)
+    for i in (2, 3, 6, 7, 8, 9, 11, 12, 13):
+        a[i] = None
+    assert ffn(cfg, a, ws=None) == B.MOE_ERR_WORKSPACE
+    assert ffn(cfg, a, n=16) == B.MOE_ERR_WORKSPACE
+    assert ffn(cfg, a, ws=FAKE + (1 << 40) + 8) == B.MOE_ERR_WORKSPACE   # not 256-aligned
+    b = list(a)
+    b[10] = args[0] + 64          # out inside hidden
+    assert ffn(cfg, b) == B.MOE_ERR_OVERLAP
+    c = list(a)
+    c[11] = FAKE + (1 << 41)      # shared_out without a shared expert
+    assert ffn(cfg, c) == B.MOE_ERR_INVALID_ARG
+    f16 = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
+    f16.dtype = 2
+    assert ffn(f16, a) == B.MOE_ERR_UNSUPPORTED
+    forced = B.ffn_cfg(I.CONFIGS["tiny_fp32"], "indexed")
+    assert ffn(forced, a) == B.MOE_ERR_UNSUPPORTED

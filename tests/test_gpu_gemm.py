@@ -1,0 +1,103 @@
+"""Grouped GEMM kernels (moe_grouped_gemm, moe_grouped_gemm_swiglu) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_ffn_moerouter_amd import binding as B
+from moe_testlib import assert_close, guarded, np64, say
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _offsets(sizes):
+    return torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int32,
+                        device="cuda")
+
+
+SEGMENTS = {
+    "ragged": [0, 1, 127, 128, 129, 300, 0, 45],
+    "one_expert_many_tiles": [1000],
+    "tiny": [3, 0, 5],
+    "uniform256": [256] * 12,
+}
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("seg", sorted(SEGMENTS))
+@pytest.mark.parametrize("shape", [(256, 384), (200, 136), (72, 40)])  # (K, N)
+@pytest.mark.parametrize("bias", [False, True])
+def test_grouped_gemm(dt, seg, shape, bias):
+    Kd, N = shape
+    sizes = SEGMENTS[seg]
+    E, M = len(sizes), int(sum(sizes))
+    say(f"[gemm] dt={dt} seg={seg} K={Kd} N={N} bias={bias}")
+    g = torch.Generator(device="cuda").manual_seed(1)
+    a = torch.randn((M, Kd), device="cuda", generator=g).to(DT[dt])
+    b = (0.1 * torch.randn((E, N, Kd), device="cuda", generator=g)).to(DT[dt])
+    bb = (0.1 * torch.randn((E, N), device="cuda", generator=g)).to(DT[dt]) if bias else None
+    off = _offsets(sizes)
+    for out_dt in ([DT[dt], torch.float32] if dt == "bf16" else [torch.float32]):
+        out, check = guarded((M, N), out_dt)
+        B.moe_grouped_gemm(a, b, off, bb, out_dtype=out_dt, out=out)
+        torch.cuda.synchronize()
+        check()
+        ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(),
+                             None if bb is None else np64(bb),
+                             "f32" if out_dt == torch.float32 else dt)
+        # a float32 output is held to the float32 bound whatever the operand dtype
+        assert_close(np64(out), ref, "f32" if out_dt == torch.float32 else dt, f"gemm {seg}")
+
+
+ACTS = {"silu_and_mul": "silu_and_mul", "swigluoai": "swigluoai",
+        "custom_clamped": ("stacked", 1.3, 0.25, 2.0),
+        "interleaved_noclamp": ("interleaved", 0.8, -0.5, 0.0)}
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("seg", ["ragged", "uniform256"])
+@pytest.mark.parametrize("act", sorted(ACTS))
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_gemm_swiglu(dt, seg, act, gather):
+    sizes = SEGMENTS[seg]
+    E, M = len(sizes), int(sum(sizes))
+    H, F = 200, 96  # ragged K tile (200 = 3*64 + 8) and ragged act tile (96 = 64 + 32)
+    say(f"[gemm-act] dt={dt} seg={seg} act={act} gather={gather}")
+    g = torch.Generator(device="cuda").manual_seed(2)
+    T = max(1, M // 3 + 1)
+    src = (3.0 * torch.randn((T if gather else M, H), device="cuda", generator=g)).to(DT[dt])
+    w = (0.2 * torch.randn((E, 2 * F, H), device="cuda", generator=g)).to(DT[dt])
+    bias = (0.5 * torch.randn((E, 2 * F), device="cuda", generator=g)).to(DT[dt])
+    off = _offsets(sizes)
+    rows = None
+    if gather:
+        rows = torch.randint(0, T * 3, (M,), device="cuda", generator=g).to(torch.int32)
+        rows = torch.clamp(rows, max=T * 3 - 1)
+    out, check = guarded((M, F), DT[dt])
+    B.moe_grouped_gemm_swiglu(src, w, off, ACTS[act], bias, a_rows=rows, a_rows_div=3,
+                              M=M, out=out)
+    torch.cuda.synchronize()
+    check()
+    a_np = np64(src)
+    if gather:
+        a_np = a_np[rows.cpu().numpy() // 3]
+    ref = O.grouped_gemm_act(a_np, np64(w), off.cpu().numpy(), ACTS[act], np64(bias), dt)
+    assert_close(np64(out), ref, dt, f"swiglu {act}")
+    if act == "swigluoai":  # the clamp must actually have fired in this case
+        h = O.grouped_gemm(a_np, np64(w), off.cpu().numpy(), np64(bias), "f64")
+        assert np.max(h[:, 0::2]) > 7.0 and np.min(h[:, 1::2]) < -7.0
+
+
+def test_gemm_large_expert_rows():
+    """Rows beyond 2^16 and offsets starting past row 0."""
+    say("[gemm] large M")
+    sizes = [0, 70000, 5]
+    E, M = 3, 70005
+    a = torch.randn((M, 64), device="cuda").to(torch.bfloat16)
+    b = (0.1 * torch.randn((E, 64, 64), device="cuda")).to(torch.bfloat16)
+    off = _offsets(sizes)
+    out = B.moe_grouped_gemm(a, b, off)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(), None, "bf16")
+    assert_close(np64(out), ref, "bf16", "large M")
