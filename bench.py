@@ -111,7 +111,7 @@ def cpu_baseline(cfg, d, budget_s: float):
               b_down=host.get("b_down"), shared_w_gate_up=host.get("shared_w_gate_up"),
               shared_w_down=host.get("shared_w_down"))
     n = min(cfg.T, 64)
-    while True:
+    while True:  # grow the sample until one pass takes a third of the budget
         t0 = time.perf_counter()
         O.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
                           host["w_down"], **kw)
@@ -119,9 +119,17 @@ def cpu_baseline(cfg, d, budget_s: float):
         if dt >= budget_s / 3 or n >= cfg.T:
             break
         n = min(cfg.T, n * 4)
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens of the same workload, float64 numpy "
-                      f"oracle, {dt:.1f} s wall"}
+    passes, total = 1, dt
+    while total < budget_s / 2:  # whole workload is quick: repeat it to about 10 s
+        t0 = time.perf_counter()
+        O.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
+                          host["w_down"], **kw)
+        total += time.perf_counter() - t0
+        passes += 1
+    return {"value": n * passes / total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} of {cfg.T} tokens of the same workload, {passes} pass(es), "
+                      f"float64 numpy oracle, {total:.1f} s wall"}
 
 
 def main():

@@ -24,7 +24,8 @@
  *     call that returns an error has launched nothing and written nothing. An output
  *     that overlaps an input returns MOE_ERR_OVERLAP before any write ([TO]
  *     MoEPostPermuteFwdOp, MoEGroupedGemmFwdOp: overlap is rejected before writing).
- *   - Sizes of zero (T == 0, M == 0) return MOE_OK and launch nothing.
+ *   - Sizes of zero (T == 0, M == 0) return MOE_OK and launch nothing (moe_permute
+ *     still writes its E+1 zero offsets); pointers to zero-sized buffers may be NULL.
  *   - dtypes: operands are MOE_F32 or MOE_BF16 (the same dtype for activations and
  *     weights); router logits and routing weights are float32.
  */

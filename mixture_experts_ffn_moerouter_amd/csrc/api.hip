@@ -140,8 +140,8 @@ int moe_abi_version(void) { return 1; }
 int moe_route(const float* logits, int64_t T, int64_t E, const float* correction_bias,
               const int32_t* expert_ids, const moe_route_cfg* cfg, float* topk_weights,
               int32_t* topk_ids, void* router_probs, void* weight_scale, void* stream) {
-  if (!logits || !topk_weights || !topk_ids || !cfg) return MOE_ERR_INVALID_ARG;
-  if (T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (!cfg || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_weights || !topk_ids)) return MOE_ERR_INVALID_ARG;
   if (E > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
   if ((router_probs == nullptr) != (weight_scale == nullptr)) return MOE_ERR_INVALID_ARG;
   int st = check_route_cfg(cfg, E, router_probs != nullptr);
@@ -181,9 +181,9 @@ int moe_route(const float* logits, int64_t T, int64_t E, const float* correction
 int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
                 int32_t* expert_offsets, int32_t* sorted_route, int32_t* route_pos,
                 const void* hidden, int64_t H, int32_t dt, void* permuted, void* stream) {
-  if (!topk_ids || !expert_offsets || !sorted_route || !route_pos) return MOE_ERR_INVALID_ARG;
-  if (T < 0 || K < 1 || E < 1) return MOE_ERR_INVALID_ARG;
-  if ((hidden == nullptr) != (permuted == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets || T < 0 || K < 1 || E < 1) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!topk_ids || !sorted_route || !route_pos)) return MOE_ERR_INVALID_ARG;
+  if ((hidden == nullptr) != (permuted == nullptr) && T > 0) return MOE_ERR_INVALID_ARG;
   if (hidden && (H < 1 || !operand_dt_ok(dt))) return MOE_ERR_INVALID_ARG;
   if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
   if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
@@ -206,8 +206,8 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
                                int64_t E, int64_t Nw, bool act_on, const moe_act_cfg* act,
                                const int32_t* offsets, int32_t dt, int32_t out_dt, void* out,
                                void* stream) {
-  if (!a || !b || !offsets || !out) return MOE_ERR_INVALID_ARG;
-  if (M < 0 || Kd < 1 || E < 1 || Nw < 1) return MOE_ERR_INVALID_ARG;
+  if (!b || !offsets || M < 0 || Kd < 1 || E < 1 || Nw < 1) return MOE_ERR_INVALID_ARG;
+  if (M > 0 && (!a || !out)) return MOE_ERR_INVALID_ARG;
   if (a_rows && a_rows_div < 1) return MOE_ERR_INVALID_ARG;
   if (act_on && !act_ok(act)) return MOE_ERR_INVALID_ARG;
   if (!operand_dt_ok(dt) || !(out_dt == dt || out_dt == MOE_F32)) return MOE_ERR_UNSUPPORTED;
@@ -268,8 +268,8 @@ int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, i
 int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
                 const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
                 void* out, int32_t out_dt, void* stream) {
-  if (!y || !topk_weights || !route_pos || !out) return MOE_ERR_INVALID_ARG;
   if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!y || !topk_weights || !route_pos || !out)) return MOE_ERR_INVALID_ARG;
   if (!operand_dt_ok(y_dt) || !any_dt_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
   if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   const size_t R = (size_t)(T * K);
@@ -301,8 +301,9 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
   int st = check_ffn_cfg(cfg);
   if (st) return st;
   const moe_ffn_cfg& c = *cfg;
-  if (!hidden || !logits || !w_gate_up || !w_down || !out) return MOE_ERR_INVALID_ARG;
-  if (c.F_shared > 0 && (!shared_w_gate_up || !shared_w_down || !shared_out))
+  if (!w_gate_up || !w_down) return MOE_ERR_INVALID_ARG;
+  if (c.T > 0 && (!hidden || !logits || !out)) return MOE_ERR_INVALID_ARG;
+  if (c.F_shared > 0 && (!shared_w_gate_up || !shared_w_down || (c.T > 0 && !shared_out)))
     return MOE_ERR_INVALID_ARG;
   if (c.F_shared == 0 && shared_out) return MOE_ERR_INVALID_ARG;
   const int backend = backend_for(c, b_gate_up || b_down);
