@@ -161,11 +161,16 @@ int moe_route(const float* logits, int64_t T, int64_t E, const float* correction
  * route_pos       [R] int32 out: inverse of sorted_route (permuted row of route r).
  * hidden, permuted  optional (both NULL or both given): permuted[m] =
  *                 hidden[sorted_route[m] / K], rows of H elements of dtype dt.
- * Limits: E <= 1024, R < 2^31. Errors: INVALID_ARG, OVERLAP.
+ * workspace       device scratch of at least moe_permute_workspace_size(T, K, E) bytes
+ *                 (per-workgroup expert counts); contents on entry do not matter.
+ * Limits: E <= 1024, R < 2^31. Errors: INVALID_ARG, OVERLAP, WORKSPACE.
+ * moe_permute_workspace_size: host only; 0 for invalid sizes.
  * ------------------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int64_t T, int64_t K, int64_t E);
 int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
                 int32_t* expert_offsets, int32_t* sorted_route, int32_t* route_pos,
-                const void* hidden, int64_t H, int32_t dt, void* permuted, void* stream);
+                const void* hidden, int64_t H, int32_t dt, void* permuted, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_grouped_gemm_swiglu - grouped gate_up GEMM with the gated activation in its
@@ -182,7 +187,9 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
  *                 expert_offsets[e+1]-1 (non-decreasing, expert_offsets[E] <= M).
  * out             [M, F] dt: act(a W_e^T + b_e) rounded to dt (ties to even). Rows not
  *                 covered by any expert are left unwritten.
- * Accumulation is float32. Limits: H % 8 == 0 for bf16 (16-byte rows), E <= 1024.
+ * Accumulation is float32. Limits: H % 8 == 0 for bf16 (16-byte rows), E <= 1024; for
+ * bf16, M*H*2 and 2F*H*2 below 2^31 bytes (32-bit offsets; a gathered source must also
+ * stay below 2^31 bytes).
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP (out vs a, weights, bias, offsets, a_rows).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows_div,
@@ -200,7 +207,8 @@ int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows
  * b               [E, N, K] dt.   bias  [E, N] dt or NULL.
  * out             [M, N] in out_dt (dt or MOE_F32). Rows outside every expert are left
  *                 unwritten.
- * Limits: K % 8 == 0 for bf16, E <= 1024. Errors: INVALID_ARG, UNSUPPORTED, OVERLAP.
+ * Limits: K % 8 == 0 for bf16, E <= 1024, M*K*2 and N*K*2 below 2^31 bytes for bf16.
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP.
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, int64_t M,
                      int64_t K, const void* b, const void* bias, int64_t E, int64_t N,

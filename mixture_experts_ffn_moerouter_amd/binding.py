@@ -27,7 +27,8 @@ BACKENDS = {"auto": 0, "staged": 1, "indexed": 2}
 ACTIVATIONS = {"silu_and_mul": (0, 1.0, 0.0, 0.0), "swigluoai": (1, 1.702, 1.0, 7.0)}
 
 # Every symbol include/moe.h declares.
-SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute",
+SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute_workspace_size",
+           "moe_permute",
            "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
            "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward")
 
@@ -79,8 +80,11 @@ def lib():
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [_P, _I64, _I64, _P, _P, ctypes.POINTER(MoeRouteCfg), _P, _P,
                                 _P, _P, _P]
+        L.moe_permute_workspace_size.restype = ctypes.c_size_t
+        L.moe_permute_workspace_size.argtypes = [_I64, _I64, _I64]
         L.moe_permute.restype = ctypes.c_int
-        L.moe_permute.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _I32, _P, _P]
+        L.moe_permute.argtypes = [_P, _I64, _I64, _I64, _P, _P, _P, _P, _I64, _I32, _P, _P,
+                                  ctypes.c_size_t, _P]
         L.moe_grouped_gemm_swiglu.restype = ctypes.c_int
         L.moe_grouped_gemm_swiglu.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _I64, _I64,
                                               _P, _I32, ctypes.POINTER(MoeActCfg), _P, _P]
@@ -168,8 +172,13 @@ def moe_route(logits, cfg: MoeRouteCfg, correction_bias=None, expert_ids=None,
     return topk_weights, topk_ids, router_probs, weight_scale
 
 
+def moe_permute_workspace_size(T: int, K: int, E: int) -> int:
+    return lib().moe_permute_workspace_size(T, K, E)
+
+
 def moe_permute(topk_ids, num_experts: int, hidden=None, expert_offsets=None,
-                sorted_route=None, route_pos=None, permuted=None, stream=None):
+                sorted_route=None, route_pos=None, permuted=None, workspace=None,
+                stream=None):
     T, K = topk_ids.shape
     R = T * K
     dev = topk_ids.device
@@ -185,9 +194,13 @@ def moe_permute(topk_ids, num_experts: int, hidden=None, expert_offsets=None,
         dt = TORCH_DTYPES[hidden.dtype]
         permuted = torch.empty((R, H), dtype=hidden.dtype, device=dev) if permuted is None \
             else permuted
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_permute_workspace_size(T, K, num_experts)),
+                                dtype=torch.uint8, device=dev)
     _check("moe_permute", lib().moe_permute(
         _ptr(topk_ids), T, K, num_experts, _ptr(expert_offsets), _ptr(sorted_route),
-        _ptr(route_pos), _ptr(hidden), H, dt, _ptr(permuted), _stream(stream)))
+        _ptr(route_pos), _ptr(hidden), H, dt, _ptr(permuted), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
     return expert_offsets, sorted_route, route_pos, permuted
 
 

@@ -2,7 +2,7 @@
 // launch order of each entry point declared in include/moe.h.
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {
@@ -72,7 +72,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Workspace carve-up of moe_ffn_forward (both backends use the same layout).
 struct FfnWs {
-  size_t topk_w, topk_ids, offsets, sorted, pos, active, act, y, shared_act, total;
+  size_t topk_w, topk_ids, offsets, sorted, pos, active, blk_cnt, act, y, shared_act, total;
 };
 
 FfnWs ffn_ws_layout(const moe_ffn_cfg& c) {
@@ -85,6 +85,7 @@ FfnWs ffn_ws_layout(const moe_ffn_cfg& c) {
   w.sorted = o; o += align256(R * 4);
   w.pos = o; o += align256(R * 4);
   w.active = o; o += align256((E + 1) * 4);
+  w.blk_cnt = o; o += align256(permute_workspace_bytes((int)R, (int)E));
   w.act = o; o += align256(R * (size_t)c.F * s);
   const size_t y_elt = s > 4 ? s : 4;  // the indexed backend keeps y in float32
   w.y = o; o += align256(R * (size_t)c.H * y_elt);
@@ -106,6 +107,12 @@ int check_ffn_cfg(const moe_ffn_cfg* c) {
   if (!act_ok(&c->act)) return MOE_ERR_INVALID_ARG;
   if (c->E > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
   if (c->dtype == MOE_BF16 && (c->H % 8 || c->F % 8 || c->F_shared % 8))
+    return MOE_ERR_UNSUPPORTED;
+  // 32-bit byte offsets inside the GEMM tiles: hidden, act and one expert's weights
+  const int64_t R = c->T * c->route.top_k, lim = (int64_t)1 << 31;
+  if (c->dtype == MOE_BF16 && (c->T * c->H * 2 >= lim || R * c->F * 2 >= lim ||
+                               2 * c->F * c->H * 2 >= lim || c->T * c->F_shared * 2 >= lim ||
+                               2 * c->F_shared * c->H * 2 >= lim))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -178,9 +185,15 @@ int moe_route(const float* logits, int64_t T, int64_t E, const float* correction
   return status_of(launch_route(a, (hipStream_t)stream));
 }
 
+size_t moe_permute_workspace_size(int64_t T, int64_t K, int64_t E) {
+  if (T < 0 || K < 1 || E < 1 || E > kMaxGemmE || T * K >= ((int64_t)1 << 31)) return 0;
+  return align256(permute_workspace_bytes((int)(T * K), (int)E));
+}
+
 int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
                 int32_t* expert_offsets, int32_t* sorted_route, int32_t* route_pos,
-                const void* hidden, int64_t H, int32_t dt, void* permuted, void* stream) {
+                const void* hidden, int64_t H, int32_t dt, void* permuted, void* workspace,
+                size_t workspace_bytes, void* stream) {
   if (!expert_offsets || T < 0 || K < 1 || E < 1) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!topk_ids || !sorted_route || !route_pos)) return MOE_ERR_INVALID_ARG;
   if ((hidden == nullptr) != (permuted == nullptr) && T > 0) return MOE_ERR_INVALID_ARG;
@@ -189,13 +202,15 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
   if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   const size_t R = (size_t)(T * K);
   const size_t row = hidden ? (size_t)H * dt_size(dt) : 0;
+  const size_t ws_need = align256(permute_workspace_bytes((int)R, (int)E));
+  if (!workspace || workspace_bytes < ws_need) return MOE_ERR_WORKSPACE;
   Range ins[] = {{topk_ids, R * 4}, {hidden, (size_t)T * row}};
   Range outs[] = {{expert_offsets, (size_t)(E + 1) * 4}, {sorted_route, R * 4},
-                  {route_pos, R * 4}, {permuted, R * row}};
-  if (any_overlap(outs, 4, ins, 2)) return MOE_ERR_OVERLAP;
+                  {route_pos, R * 4}, {permuted, R * row}, {workspace, ws_need}};
+  if (any_overlap(outs, 5, ins, 2)) return MOE_ERR_OVERLAP;
   hipStream_t s = (hipStream_t)stream;
   int st = status_of(launch_permute(topk_ids, (int)R, (int)E, expert_offsets, sorted_route,
-                                    route_pos, nullptr, s));
+                                    route_pos, nullptr, (int32_t*)workspace, s));
   if (st || !hidden || R == 0) return st;
   return status_of(launch_gather_rows(hidden, sorted_route, (int)K, (int)R, (int64_t)row,
                                       permuted, s));
@@ -215,6 +230,9 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   if (M >= ((int64_t)1 << 31) || Nw >= ((int64_t)1 << 30) || Kd >= ((int64_t)1 << 30))
     return MOE_ERR_UNSUPPORTED;
   if (dt == MOE_BF16 && Kd % 8) return MOE_ERR_UNSUPPORTED;
+  // bf16 tiles address A and one expert's weights with 32-bit byte offsets
+  if (dt == MOE_BF16 && (M * Kd * 2 >= ((int64_t)1 << 31) || Nw * Kd * 2 >= ((int64_t)1 << 31)))
+    return MOE_ERR_UNSUPPORTED;
   if (dt == MOE_F32 && Kd > 12288) return MOE_ERR_UNSUPPORTED;  // A row staged in LDS
   const int64_t Nout = act_on ? Nw / 2 : Nw;
   const size_t s = dt_size(dt);
@@ -368,7 +386,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
   // 2. permute (expert-contiguous order; active-expert list for the indexed backend)
   if ((st = status_of(launch_permute(topk_ids, R, (int)E, offsets, sorted, pos,
                                      backend == MOE_BACKEND_INDEXED ? active : nullptr,
-                                     strm))))
+                                     (int32_t*)(ws + w.blk_cnt), strm))))
     return st;
   int y_dt = c.dtype;
   if (backend == MOE_BACKEND_INDEXED) {

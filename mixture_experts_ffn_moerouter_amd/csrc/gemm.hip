@@ -10,28 +10,46 @@
 //      L = clamp(l, -limit, limit), G * sigmoid(alpha G) * (L + beta), float math,
 //      limit <= 0 disables both clamps.
 //
-// bf16 kernel: a 128 x 128 output tile per 256-thread workgroup, K in steps of 64 staged
-// through LDS (double-buffered: the next step's global loads are in flight while the
-// current step runs on the matrix cores), v_mfma_f32_32x32x16_bf16 with each wave owning
-// a 64 x 64 sub-tile. For the gated activation the tile's 128 weight rows are 64 gate
-// rows and the 64 matching up rows, placed in LDS so that a lane's gate and up
-// accumulators hold the same output element; the epilogue pairs them directly. Rows of A
-// may be gathered (a_rows), so the permuted activation copy is never materialised.
+// bf16 kernel, templated on the tile shape: RB and CB 32-row blocks of token rows and of
+// weight rows per wave, waves arranged 2 x 2, so a tile is 64*RB token rows x 64*CB weight
+// rows, K in steps of 64 (v_mfma_f32_32x32x16_bf16, float32 accumulators). The shape in
+// use is 128 x 128 with two workgroups (eight waves) per CU. Weight streaming from HBM
+// bounds these shapes, so the loop keeps the loads of the next two K steps in flight in
+// registers (token rows PA steps ahead, weights two) while the matrix cores work on the
+// step held in LDS; LDS is double buffered (row stride 72 elements: conflict-free 16-byte
+// fragment reads), and each load instruction reads whole 128-byte row segments. For the
+// gated activation the tile's weight rows are gate rows and the matching up rows, placed
+// so that a lane's gate and up accumulators hold the same output element; the epilogue
+// pairs them directly. Rows of A may be gathered (a_rows), so the permuted activation
+// copy is never materialised. Loads use buffer resources (32-bit offsets from a scalar
+// base); out-of-range pieces (rows past the tile, weight rows past N, the K tail, steps
+// past the end) get an offset past the buffer's range so the hardware returns zeros
+// without a branch, which keeps the compiler's wait counts of the pipeline exact.
 //
-// Tile map: the number of 128-row tiles of each expert comes from expert_offsets on the
-// device (no host synchronisation). The grid is an upper bound; every workgroup rebuilds
-// the map in LDS, picks its (tile, n-tile) and leaves if it has none. Consecutive logical
-// tiles go to the same XCD (workgroups are dealt round-robin over the 8 XCDs), so the
-// n-tiles that share one A tile run close together on one L2.
+// Tile map: an expert with M_e rows gets ceil(M_e / (64*RB)) tiles of equal height
+// (rounded up to 32 rows); a wave's K loop is compiled for its count of live row blocks.
+// Tile counts come from expert_offsets on the device (no host synchronisation); the grid
+// is an upper bound, every workgroup rebuilds the map in LDS, picks its (tile, n-tile)
+// and leaves if it has none. Consecutive logical tiles go to the same XCD (workgroups are
+// dealt round-robin over the 8 XCDs) and are ordered expert, n-tile, row tile: the row
+// tiles sharing a weight slice run side by side on one L2, and so do the n-tiles sharing
+// the expert's token rows.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride in elements
+constexpr int BK = 64, LDK = BK + 8;      // K step; LDS row stride in elements
 constexpr int NT = 256;
 constexpr int kMaxE = 1024;
 constexpr int kXcd = 8;
+// Tile shape: RB 32-row blocks of token rows and CB 32-row blocks of weight rows per wave;
+// waves (wm, wn) are 2 x 2, so a tile holds 64*RB token rows and 64*CB weight rows.
+template <int RB, int CB> constexpr int stage_elems() { return (64 * RB + 64 * CB) * LDK; }
+template <int RB, int CB> constexpr size_t lds_bytes() { return (size_t)2 * stage_elems<RB, CB>() * 2; }
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
 
 __device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float beta,
                                           float limit) {
@@ -42,18 +60,25 @@ __device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float b
   return g * (1.0f / (1.0f + __expf(-alpha * g))) * (l + beta);
 }
 
-// Builds s_pre[0..E] = exclusive prefix of per-expert tile counts (and copies the
-// offsets into s_off). Called by all NT threads.
-// offsets == NULL means one expert that owns rows 0 .. M-1.
+// Tiles of an expert with `rows` rows, and the rows per tile (a multiple of 32).
+__device__ __forceinline__ int tiles_of(int rows, int bm) { return (rows + bm - 1) / bm; }
+__device__ __forceinline__ int rows_per_tile(int rows, int bm) {
+  const int n = tiles_of(rows, bm);
+  return n ? ((rows + n - 1) / n + 31) / 32 * 32 : 0;
+}
+
+// Builds s_pre[0..E] = exclusive prefix of per-expert tile counts and copies the offsets
+// into s_off. offsets == NULL means one expert that owns rows 0 .. M-1. All NT threads.
 __device__ void build_tile_map(const int32_t* offsets, int E, int M, int bm, int* s_off,
                                int* s_pre, int* s_tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int W = NT / 64;
   for (int i = tid; i <= E; i += NT) s_off[i] = offsets ? offsets[i] : (i == 0 ? 0 : M);
   __syncthreads();
   int carry = 0;
   for (int e0 = 0; e0 < E; e0 += NT) {
     const int e = e0 + tid;
-    const int c = e < E ? (s_off[e + 1] - s_off[e] + bm - 1) / bm : 0;
+    const int c = e < E ? tiles_of(s_off[e + 1] - s_off[e], bm) : 0;
     int x = c;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -62,9 +87,12 @@ __device__ void build_tile_map(const int32_t* offsets, int E, int M, int bm, int
     }
     if (lane == 63) s_tmp[wave] = x;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += s_tmp[w];
-    const int chunk = s_tmp[0] + s_tmp[1] + s_tmp[2] + s_tmp[3];
+    int wbase = 0, chunk = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      wbase += w < wave ? s_tmp[w] : 0;
+      chunk += s_tmp[w];
+    }
     if (e < E) s_pre[e] = carry + wbase + x - c;
     carry += chunk;
     __syncthreads();
@@ -83,155 +111,259 @@ __device__ __forceinline__ int find_expert(const int* s_pre, int E, int tile) {
   return lo;
 }
 
-template <bool ACT, int LAYOUT, bool OUT_F32>
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ int s_tmp[8];
-  extern __shared__ __align__(16) uint16_t smem[];  // [2][BM + BN][LDK]
-  // The tile map lives in the tile buffers until the K loop starts.
-  int* s_off = (int*)smem;
+__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+template <int RB, int CB, int PA, bool ACT, int LAYOUT, bool OUT_F32>
+__global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int BMX = 64 * RB, BNW = 64 * CB;
+  constexpr int NLD = (BMX * BK / 8) / NT, NLDB = (BNW * BK / 8) / NT;
+  constexpr int kStageElems = stage_elems<RB, CB>();
+  static_assert(lds_bytes<RB, CB>() >= 2 * (kMaxE + 1) * sizeof(int), "tile map alias");
+  static_assert(CB == 2 || CB == 4, "weight blocks per wave");
+  __shared__ int s_tmp[NT / 64];
+  extern __shared__ __align__(16) uint16_t smem[];  // [2][BMX + BNW][LDK]
+  int* s_off = (int*)smem;  // the tile map lives in the stage buffers until the K loop
   int* s_pre = s_off + kMaxE + 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = g.E;
-  build_tile_map(g.offsets, E, g.M, BM, s_off, s_pre, s_tmp);
+  build_tile_map(g.offsets, E, g.M, BMX, s_off, s_pre, s_tmp);
 
-  const int n_tiles_n = ACT ? (g.Nout + BN / 2 - 1) / (BN / 2) : (g.Nw + BN - 1) / BN;
+  const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
   const int n_valid = s_pre[E] * n_tiles_n;
   const int per = (n_valid + kXcd - 1) / kXcd;
   const int slot = blockIdx.x / kXcd;
   const int L = (blockIdx.x % kXcd) * per + slot;
-  if (slot >= per || L >= n_valid) return;
-  const int tile = L / n_tiles_n, nt = L % n_tiles_n;
-  const int e = find_expert(s_pre, E, tile);
-  const int m0 = s_off[e] + (tile - s_pre[e]) * BM;
-  const int m1 = min(m0 + BM, s_off[e + 1]);
+  if (slot >= per || L >= n_valid) return;  // uniform per workgroup
+  // Logical order: expert, then n-tile, then row tile, so the row tiles that share one
+  // weight slice are adjacent (they run side by side on one XCD and the weight lines are
+  // fetched from HBM once); expert e owns [s_pre[e], s_pre[e+1]) * n_tiles_n.
+  const int e = find_expert(s_pre, E, L / n_tiles_n);
+  const int t_e = s_pre[e + 1] - s_pre[e];
+  const int local = L - s_pre[e] * n_tiles_n;
+  const int nt = local / t_e, mt = local % t_e;
+  const int rpt = rows_per_tile(s_off[e + 1] - s_off[e], BMX);
+  const int m0 = s_off[e] + mt * rpt;
+  const int m1 = min(m0 + rpt, s_off[e + 1]);
+  const int rows = m1 - m0;
+  const int nb = (rows + 31) / 32;  // live 32-row blocks
   const int Kd = g.Kd;
-  __syncthreads();  // every thread has read the map; the buffers become tiles
+  __syncthreads();  // every thread has read the map; the buffers become stages
 
-  // ---- per-thread global source rows (4 A vectors, 4 B vectors of 8 elements)
-  const uint16_t* pa[4];
-  const uint16_t* pb[4];
-  int kv[4], lrow[4];
-  const uint16_t* A = (const uint16_t*)g.a;
-  const uint16_t* B = (const uint16_t*)g.b + (int64_t)e * g.Nw * Kd;
+  // ---- loads: thread tid moves 16-byte piece (tid & 7) of rows (tid >> 3) + 32 i, i < NLD,
+  // of both the A and the B tile (8 consecutive lanes read one 128-byte row segment).
+  const int kc = (tid & 7) * 8;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, 0x7fffffff, 0x00020000);
+  const uint16_t* Bexp = (const uint16_t*)g.b + (int64_t)e * g.Nw * Kd;
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Bexp, (short)0, (int)((int64_t)g.Nw * Kd * 2), 0x00020000);
+  uint32_t aoff[NLD], boff[NLDB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + NT * i;
-    lrow[i] = v >> 3;
-    kv[i] = (v & 7) * 8;
-    int m = min(m0 + lrow[i], m1 - 1);
-    int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
-    pa[i] = A + (int64_t)src * Kd + kv[i];
-    int r = lrow[i], wr;
+  for (int i = 0; i < NLD; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    const bool aon = r < rows;
+    const int m = m0 + (aon ? r : 0);
+    const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
+    aoff[i] = aon ? ((uint32_t)src * (uint32_t)Kd + kc) * 2u : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < NLDB; ++i) {
+    const int r = (tid >> 3) + 32 * i;
+    int wr;
+    bool bon;
     if (ACT) {
-      const int j = min(nt * (BN / 2) + (r & (BN / 2 - 1)), g.Nout - 1);
-      const bool up = r >= BN / 2;
+      const int j = nt * (BNW / 2) + (r & (BNW / 2 - 1));
+      const bool up = r >= BNW / 2;
+      bon = j < g.Nout;
       wr = LAYOUT == 0 ? (up ? g.Nout + j : j) : (2 * j + (up ? 1 : 0));
     } else {
-      wr = min(nt * BN + r, g.Nw - 1);
+      wr = nt * BNW + r;
+      bon = wr < g.Nw;
     }
-    pb[i] = B + (int64_t)wr * Kd + kv[i];
+    boff[i] = bon ? ((uint32_t)wr * (uint32_t)Kd + kc) * 2u : kOOB;
   }
 
-  bf16x8 ra[4], rb[4];
-  auto load_global = [&](int k0) {
+  // A (token rows, mostly from L2) is prefetched PA K steps ahead, the weights (from HBM)
+  // two: sa0/sa1 hold A of the next step(s), sb0/sb1 the weights of the next two.
+  bf16x8 sa0[NLD], sa1[PA == 2 ? NLD : 1], sb0[NLDB], sb1[NLDB];
+  auto load_a = [&](int k0, bf16x8* xa) {
+    const bool kin = k0 + kc < Kd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool in = k0 + kv[i] < Kd;
-      ra[i] = in ? *(const bf16x8*)(pa[i] + k0) : bf16x8{};
-      rb[i] = in ? *(const bf16x8*)(pb[i] + k0) : bf16x8{};
-    }
+    for (int i = 0; i < NLD; ++i) xa[i] = buf_load16(ra, kin ? aoff[i] + 2u * (uint32_t)k0 : kOOB);
   };
-  auto store_lds = [&](int buf) {
-    uint16_t* sa = smem + buf * (BM + BN) * LDK;
-    uint16_t* sb = sa + BM * LDK;
+  auto load_b = [&](int k0, bf16x8* xb) {
+    const bool kin = k0 + kc < Kd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(bf16x8*)(sa + lrow[i] * LDK + kv[i]) = ra[i];
-      *(bf16x8*)(sb + lrow[i] * LDK + kv[i]) = rb[i];
-    }
+    for (int i = 0; i < NLDB; ++i) xb[i] = buf_load16(rb, kin ? boff[i] + 2u * (uint32_t)k0 : kOOB);
+  };
+  auto store_stage = [&](int buf, const bf16x8* xa, const bf16x8* xb) {
+    uint16_t* la = smem + buf * kStageElems;
+    uint16_t* lb = la + BMX * LDK;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) *(bf16x8*)(la + ((tid >> 3) + 32 * i) * LDK + kc) = xa[i];
+#pragma unroll
+    for (int i = 0; i < NLDB; ++i) *(bf16x8*)(lb + ((tid >> 3) + 32 * i) * LDK + kc) = xb[i];
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  const int arow0 = wm * 64 + (lane & 31);
-  int brow[2];
+  // wave (wm, wn): row blocks wm, wm+2, ... (RB of them); weight rows: for the gated activation
+  // gate rows wn*16*CB + [0,16*CB) and the matching up rows BNW/2 + the same; else
+  // wn*32*CB + [0,32*CB).
+  const int wm = wave & 1, wn = wave >> 1;
+  int brow[CB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    brow[j] = (ACT ? (j * (BN / 2) + wn * 32) : (wn * 64 + j * 32)) + (lane & 31);
+  for (int j = 0; j < CB; ++j)
+    brow[j] = (ACT ? ((j / (CB / 2)) * (BNW / 2) + wn * 16 * CB + (j % (CB / 2)) * 32)
+                   : (wn * 32 * CB + j * 32)) +
+              (lane & 31);
   const int kq = (lane >> 5) * 8;
+  const int nbw = (nb - wm + 1) / 2;  // live row blocks of this wave
 
-  f32x16 acc[2][2];
+  f32x16 acc[RB][CB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
 
-  const int nk = (Kd + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_global((kt + 1) * BK);
-    const uint16_t* sa = smem + (kt & 1) * (BM + BN) * LDK;
-    const uint16_t* sb = sa + BM * LDK;
+  // The K loop, compiled once per count of live row blocks so that every fragment read
+  // of a sub-step is issued before its MFMAs.
+  auto main_loop = [&](auto nbw_c) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    auto compute = [&](int buf) {
+      const uint16_t* sa = smem + buf * kStageElems;
+      const uint16_t* sb = sa + BMX * LDK;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[2], fb[2];
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        bf16x8 fb[CB], fa[NBW];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *(const bf16x8*)(sa + (arow0 + i * 32) * LDK + ks * 16 + kq);
+        for (int j = 0; j < CB; ++j) fb[j] = *(const bf16x8*)(sb + brow[j] * LDK + ks * 16 + kq);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *(const bf16x8*)(sb + brow[j] * LDK + ks * 16 + kq);
+        for (int i = 0; i < NBW; ++i)
+          fa[i] = *(const bf16x8*)(sa + ((wm + 2 * i) * 32 + (lane & 31)) * LDK + ks * 16 + kq);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NBW; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < CB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    // Step s uses LDS buffer s % 2 and weight set sb[s % 2] (and, with PA = 2, A set
+    // sa[s % 2]). After storing step k+1 the loads of the steps two ahead (PA = 2: A and
+    // weights of k+3) or A of k+2 and then the weights of k+3 (PA = 1) are issued, so the
+    // wait before the next store leaves the newest loads in flight. Every half-iteration
+    // issues the same loads (steps past the end load nothing: their offsets are out of
+    // range), which keeps the compiler's wait counts exact.
+    const int nk = (Kd + BK - 1) / BK;
+    int k = 0;
+    if constexpr (PA == 2) {
+      load_a(0, sa0);
+      load_b(0, sb0);
+      load_a(BK, sa1);
+      load_b(BK, sb1);
+      store_stage(0, sa0, sb0);
+      load_a(2 * BK, sa0);
+      load_b(2 * BK, sb0);
+      __syncthreads();
+      for (; k + 1 < nk; k += 2) {
+        compute(0);
+        store_stage(1, sa1, sb1);
+        load_a((k + 3) * BK, sa1);
+        load_b((k + 3) * BK, sb1);
+        __syncthreads();
+        compute(1);
+        store_stage(0, sa0, sb0);
+        load_a((k + 4) * BK, sa0);
+        load_b((k + 4) * BK, sb0);
+        __syncthreads();
+      }
+    } else {
+      load_a(0, sa0);
+      load_b(0, sb0);
+      load_b(BK, sb1);
+      store_stage(0, sa0, sb0);
+      load_a(BK, sa0);
+      load_b(2 * BK, sb0);
+      __syncthreads();
+      for (; k + 1 < nk; k += 2) {
+        compute(0);
+        store_stage(1, sa0, sb1);
+        load_a((k + 2) * BK, sa0);
+        load_b((k + 3) * BK, sb1);
+        __syncthreads();
+        compute(1);
+        store_stage(0, sa0, sb0);
+        load_a((k + 3) * BK, sa0);
+        load_b((k + 4) * BK, sb0);
+        __syncthreads();
+      }
     }
-    if (kt + 1 < nk) store_lds((kt + 1) & 1);
-    __syncthreads();
+    if (k < nk) compute(0);  // odd number of K steps: the last one is in buffer 0
+  };
+  // With 128-row tiles the loop is compiled for 2 and for 1 live row blocks of the wave;
+  // with 256-row tiles one loop covers all 4 (blocks past the tile's last row read rows
+  // that load as zeros, and their results are not written).
+  if constexpr (RB == 2) {
+    if (nbw >= 2) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
+  } else {
+    main_loop(std::integral_constant<int, RB>{});
   }
 
   // ---- epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4
   // and column l%32 of its 32 x 32 block.
   const uint16_t* bias = (const uint16_t*)g.bias;
   if (ACT) {
-    const int j = nt * (BN / 2) + wn * 32 + (lane & 31);
-    if (j < g.Nout) {
-      float bg = 0.f, bu = 0.f;
-      if (bias) {
-        const uint16_t* be = bias + (int64_t)e * g.Nw;
-        bg = bf16_to_f32(be[LAYOUT == 0 ? j : 2 * j]);
-        bu = bf16_to_f32(be[LAYOUT == 0 ? g.Nout + j : 2 * j + 1]);
-      }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int h = 0; h < CB / 2; ++h) {  // 32-column groups of this wave's 16*CB outputs
+      const int j = nt * (BNW / 2) + wn * 16 * CB + h * 32 + (lane & 31);
+      if (j < g.Nout) {
+        float bg = 0.f, bu = 0.f;
+        if (bias) {
+          const uint16_t* be = bias + (int64_t)e * g.Nw;
+          bg = bf16_to_f32(be[LAYOUT == 0 ? j : 2 * j]);
+          bu = bf16_to_f32(be[LAYOUT == 0 ? g.Nout + j : 2 * j + 1]);
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (m < m1) {
-            float v = swiglu_f(acc[i][0][r] + bg, acc[i][1][r] + bu, g.alpha, g.beta, g.limit);
-            if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nout + j] = v;
-            else ((uint16_t*)g.out)[(int64_t)m * g.Nout + j] = f32_to_bf16(v);
+        for (int i = 0; i < RB; ++i) {
+          if (i < nbw) {
+            const int rb = wm + 2 * i;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              if (m < m1) {
+                float v = swiglu_f(acc[i][h][r] + bg, acc[i][CB / 2 + h][r] + bu, g.alpha, g.beta,
+                                   g.limit);
+                if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nout + j] = v;
+                else ((uint16_t*)g.out)[(int64_t)m * g.Nout + j] = f32_to_bf16(v);
+              }
+            }
           }
         }
+      }
     }
   } else {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int n = nt * BN + wn * 64 + jb * 32 + (lane & 31);
+    for (int jb = 0; jb < CB; ++jb) {
+      const int n = nt * BNW + wn * 32 * CB + jb * 32 + (lane & 31);
       if (n < g.Nw) {
         const float bn = bias ? bf16_to_f32(bias[(int64_t)e * g.Nw + n]) : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RB; ++i) {
+          if (i < nbw) {
+            const int rb = wm + 2 * i;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (m < m1) {
-              float v = acc[i][jb][r] + bn;
-              if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nw + n] = v;
-              else ((uint16_t*)g.out)[(int64_t)m * g.Nw + n] = f32_to_bf16(v);
+            for (int r = 0; r < 16; ++r) {
+              const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+              if (m < m1) {
+                float v = acc[i][jb][r] + bn;
+                if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nw + n] = v;
+                else ((uint16_t*)g.out)[(int64_t)m * g.Nw + n] = f32_to_bf16(v);
+              }
             }
           }
+        }
       }
     }
   }
@@ -282,18 +414,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-template <bool ACT, int LAYOUT, bool OUT_F32>
-hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
-  const int n_tiles_n = ACT ? (g.Nout + BN / 2 - 1) / (BN / 2) : (g.Nw + BN - 1) / BN;
-  const int64_t max_tiles = (g.M + BM - 1) / BM + (g.E < g.M ? g.E : g.M);
+template <int RB, int CB, int PA, bool ACT, int LAYOUT, bool OUT_F32>
+hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
+  constexpr int BMX = 64 * RB, BNW = 64 * CB;
+  const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
+  const int64_t max_tiles = (g.M + BMX - 1) / BMX + (g.E < g.M ? g.E : g.M);
   int64_t grid = max_tiles * n_tiles_n;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(uint16_t);
-  hipError_t err = hipFuncSetAttribute((const void*)gemm_bf16_kernel<ACT, LAYOUT, OUT_F32>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const auto kern = gemm_bf16_kernel<RB, CB, PA, ACT, LAYOUT, OUT_F32>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds_bytes<RB, CB>());
   if (err != hipSuccess) return err;
-  gemm_bf16_kernel<ACT, LAYOUT, OUT_F32><<<dim3((unsigned)grid), dim3(NT), lds, s>>>(g);
+  kern<<<dim3((unsigned)grid), dim3(NT), lds_bytes<RB, CB>(), s>>>(g);
   return hipGetLastError();
+}
+
+// 128 x 128 tiles, two workgroups per CU, token rows and weights both two K steps ahead:
+// of the shapes this kernel is written for (also 128 x 256 and 256 x 256 with one
+// workgroup per CU, and A one step ahead) the fastest on every workload measured.
+template <bool ACT, int LAYOUT, bool OUT_F32>
+hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
+  return launch_bf16_shape<2, 2, 2, ACT, LAYOUT, OUT_F32>(g, s);
 }
 
 }  // namespace
@@ -307,10 +449,13 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s) {
   }
   if (g.act) {
     if (g.layout == 0)
-      return g.out_dt == 0 ? launch_bf16<true, 0, true>(g, s) : launch_bf16<true, 0, false>(g, s);
-    return g.out_dt == 0 ? launch_bf16<true, 1, true>(g, s) : launch_bf16<true, 1, false>(g, s);
+      return g.out_dt == 0 ? launch_bf16<true, 0, true>(g, s)
+                           : launch_bf16<true, 0, false>(g, s);
+    return g.out_dt == 0 ? launch_bf16<true, 1, true>(g, s)
+                         : launch_bf16<true, 1, false>(g, s);
   }
-  return g.out_dt == 0 ? launch_bf16<false, 0, true>(g, s) : launch_bf16<false, 0, false>(g, s);
+  return g.out_dt == 0 ? launch_bf16<false, 0, true>(g, s)
+                       : launch_bf16<false, 0, false>(g, s);
 }
 
 }  // namespace moe

@@ -53,10 +53,13 @@ struct RouteArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
 
 // active_list: optional [E+1] int32 out; active_list[0..n) = experts with routes, in
-// ascending order, and active_list[E] = n.
+// ascending order, and active_list[E] = n. blk_cnt: device scratch of
+// permute_workspace_bytes(R, E) bytes (per-workgroup expert counts).
+int permute_chunk(int R);
+size_t permute_workspace_bytes(int R, int E);
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets,
                           int32_t* sorted_route, int32_t* route_pos, int32_t* active_list,
-                          hipStream_t s);
+                          int32_t* blk_cnt, hipStream_t s);
 hipError_t launch_gather_rows(const void* src, const int32_t* rows, int div, int M,
                               int64_t row_bytes, void* dst, hipStream_t s);
 

@@ -5,14 +5,16 @@
 //      layout (one run of rows per expert, described by segment ends). Here the runs are
 //      not padded, and inside a run the routes are in ascending route index.
 //
-// One workgroup of 16 waves does it all, so no device-wide synchronisation is needed:
-//  1. wave w counts the expert ids of its contiguous slice of routes (LDS counters);
-//  2. a block scan over experts gives expert_offsets, and per (wave, expert) the first
-//     row that wave writes for that expert;
-//  3. each wave walks its slice 64 routes at a time, in order. Lanes that carry the
-//     same expert find each other with one ballot per id bit; a lane's rank among its
-//     peers plus the running base gives its row, and the lowest peer advances the base.
-// Waves own consecutive slices and go through them in order, so the result is stable.
+// Two launches, no host synchronisation:
+//  1. count: workgroup b counts the expert ids of routes [b*chunk, (b+1)*chunk) in LDS and
+//     writes its row of the [nblk][E] count matrix;
+//  2. scatter: workgroup b reads the matrix, forms expert_offsets (exclusive scan of the
+//     column sums) and the rows that earlier workgroups take per expert, then walks its
+//     chunk: wave w takes a contiguous slice, counts it per expert, and after a scan over
+//     the waves goes through it 64 routes at a time, in order. Lanes that carry the same
+//     expert find each other with one ballot per id bit; a lane's rank among its peers
+//     plus the running base gives its row, and the lowest peer advances the base.
+// Chunks, and slices inside them, are walked in route order, so the result is stable.
 #include "moe_internal.h"
 
 namespace moe {
@@ -49,39 +51,59 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* lds_tmp, int& to
   return res;
 }
 
-__global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __restrict__ ids,
-                                                           int R, int E, int nbits,
-                                                           int32_t* offsets,
-                                                           int32_t* sorted_route,
-                                                           int32_t* route_pos,
-                                                           int32_t* active) {
+__global__ __launch_bounds__(kThreads) void permute_count_kernel(const int32_t* __restrict__ ids,
+                                                                 int R, int E, int chunk,
+                                                                 int32_t* __restrict__ blk_cnt) {
+  extern __shared__ int lds[];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E; i += kThreads) lds[i] = 0;
+  __syncthreads();
+  const int r0 = blockIdx.x * chunk, r1 = min(R, r0 + chunk);
+  for (int r = r0 + tid; r < r1; r += kThreads) atomicAdd(&lds[ids[r]], 1);
+  __syncthreads();
+  for (int i = tid; i < E; i += kThreads) blk_cnt[(int64_t)blockIdx.x * E + i] = lds[i];
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ ids, int R, int E, int nbits, int chunk, int nblk,
+    const int32_t* __restrict__ blk_cnt, int32_t* offsets, int32_t* sorted_route,
+    int32_t* route_pos, int32_t* active) {
   extern __shared__ int lds[];
   int* cnt = lds;                   // [kWaves][E]: counts, then running row bases
   int* tmp = lds + kWaves * E;      // scan scratch [2*kWaves+1]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  const int c0 = b * chunk, c1 = min(R, c0 + chunk);
 
   for (int i = tid; i < kWaves * E; i += kThreads) cnt[i] = 0;
   __syncthreads();
-  const int per = (((R + kWaves - 1) / kWaves) + 63) / 64 * 64;
-  const int r0 = min(R, wave * per), r1 = min(R, r0 + per);
+  const int per = (((c1 - c0 + kWaves - 1) / kWaves) + 63) / 64 * 64;
+  const int r0 = min(c1, c0 + wave * per), r1 = min(c1, r0 + per);
   for (int r = r0 + lane; r < r1; r += 64) atomicAdd(&cnt[wave * E + ids[r]], 1);
   __syncthreads();
 
-  // Scan over experts, in chunks of kThreads experts.
+  // Per expert: column sum over all workgroups (scanned into offsets) and the rows of the
+  // workgroups before this one; then this workgroup's per-wave bases.
   int carry = 0, carry_active = 0;
   for (int e0 = 0; e0 < E; e0 += kThreads) {
     const int e = e0 + tid;
-    int tot = 0;
+    int tot = 0, before = 0;
     if (e < E)
-      for (int w = 0; w < kWaves; ++w) tot += cnt[w * E + e];
+      for (int bb = 0; bb < nblk; ++bb) {
+        const int c = blk_cnt[(int64_t)bb * E + e];
+        tot += c;
+        before += bb < b ? c : 0;
+      }
     int chunk_total;
     int excl = block_exclusive_scan(tot, tmp, chunk_total) + carry;
     int act_total;
     int act_excl = block_exclusive_scan(tot > 0 ? 1 : 0, tmp, act_total) + carry_active;
     if (e < E) {
-      offsets[e] = excl;
-      if (active && tot > 0) active[act_excl] = e;
-      int base = excl;
+      if (b == 0) {
+        offsets[e] = excl;
+        if (active && tot > 0) active[act_excl] = e;
+      }
+      int base = excl + before;
       for (int w = 0; w < kWaves; ++w) {
         int c = cnt[w * E + e];
         cnt[w * E + e] = base;
@@ -91,23 +113,23 @@ __global__ __launch_bounds__(kThreads) void permute_kernel(const int32_t* __rest
     carry += chunk_total;
     carry_active += act_total;
   }
-  if (tid == 0) {
+  if (b == 0 && tid == 0) {
     offsets[E] = R;
     if (active) active[E] = carry_active;
   }
   __syncthreads();
 
-  // Stable scatter.
+  // Stable scatter of this wave's slice.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int rb = r0; rb < r1; rb += 64) {
     const int r = rb + lane;
     const bool on = r < r1;
     const int e = on ? ids[r] : 0;
     uint64_t peers = __ballot(on);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t m = __ballot(on && bit);
-      peers &= bit ? m : ~m;
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t m = __ballot(on && set);
+      peers &= set ? m : ~m;
     }
     if (on) {
       const int rank = __popcll(peers & lt_mask);
@@ -135,17 +157,36 @@ __global__ void gather_rows_kernel(const char* __restrict__ src, const int32_t* 
 
 }  // namespace
 
+size_t permute_workspace_bytes(int R, int E) {
+  const int chunk = permute_chunk(R);
+  const int nblk = R > 0 ? (R + chunk - 1) / chunk : 1;
+  return (size_t)nblk * E * sizeof(int32_t);
+}
+
+int permute_chunk(int R) {
+  // at least 2048 routes per workgroup, and at most 64 workgroups
+  int c = (R + 63) / 64;
+  c = (c + 1023) / 1024 * 1024;
+  return c < 2048 ? 2048 : c;
+}
+
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets,
                           int32_t* sorted_route, int32_t* route_pos, int32_t* active,
-                          hipStream_t s) {
+                          int32_t* blk_cnt, hipStream_t s) {
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  size_t lds = (size_t)(kWaves * E + 2 * kWaves + 1) * sizeof(int);
-  hipError_t err = hipFuncSetAttribute((const void*)permute_kernel,
+  const int chunk = permute_chunk(R);
+  const int nblk = R > 0 ? (R + chunk - 1) / chunk : 1;
+  const size_t lds = (size_t)(kWaves * E + 2 * kWaves + 1) * sizeof(int);
+  hipError_t err = hipFuncSetAttribute((const void*)permute_scatter_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  permute_kernel<<<1, kThreads, lds, s>>>(ids, R, E, nbits, offsets, sorted_route, route_pos,
-                                          active);
+  permute_count_kernel<<<nblk, kThreads, (size_t)E * sizeof(int), s>>>(ids, R, E, chunk,
+                                                                       blk_cnt);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  permute_scatter_kernel<<<nblk, kThreads, lds, s>>>(ids, R, E, nbits, chunk, nblk, blk_cnt,
+                                                     offsets, sorted_route, route_pos, active);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(B.SYMBOLS)
     L = B.lib()
     for n in names:
@@ -121,12 +121,22 @@ def test_gemm_combine_permute_argument_errors():
     st = L.moe_combine(FAKE, 1, FAKE + (1 << 20), FAKE + (1 << 21), 4, 2, 64, 1.0, FAKE + 32,
                        1, None)
     assert st == B.MOE_ERR_OVERLAP
+    WS = FAKE + (1 << 30)
     st = L.moe_permute(FAKE, 4, 2, 2000, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, 0, 0,
-                       None, None)
+                       None, WS, 1 << 20, None)
     assert st == B.MOE_ERR_UNSUPPORTED
     st = L.moe_permute(FAKE, 4, 2, 8, FAKE + 4, FAKE + 8192, FAKE + 12288, None, 0, 0, None,
-                       None)
+                       WS, 1 << 20, None)
     assert st == B.MOE_ERR_OVERLAP
+    need = B.moe_permute_workspace_size(4, 2, 8)
+    assert need >= 8 * 4
+    st = L.moe_permute(FAKE, 4, 2, 8, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, 0, 0,
+                       None, WS, need - 1, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    st = L.moe_permute(FAKE, 4, 2, 8, FAKE + 4096, FAKE + 8192, FAKE + 12288, None, 0, 0,
+                       None, None, need, None)
+    assert st == B.MOE_ERR_WORKSPACE
+    assert B.moe_permute_workspace_size(4, 2, 2000) == 0
 
 
 def test_ffn_argument_errors():
