@@ -1,6 +1,7 @@
 """Benchmark of the routed MoE FFN forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter scaling
 
 A step is one moe_ffn_forward over one batch: router, permute, grouped gate_up GEMM with
 the fused activation, grouped down GEMM and combine (and the shared expert when the
@@ -10,6 +11,7 @@ line. The dominant kernel (the grouped gate_up GEMM) is also timed on its own, l
 launch, with HIP events on the stream it runs on, for the roofline entry.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +29,45 @@ from mixture_experts_ffn_moerouter_amd import inputs as I  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
+
+
+# HBM bytes of one grouped gate_up launch, read by the FETCH_SIZE and WRITE_SIZE counters
+# (rocprofv3 --pmc, one counter per run, over this script's own launches) and scaled by
+# what the same counters read for a plain copy of known size (--copy-calibration). The
+# figure belongs to the kernel source it was measured on: gemm_src is the SHA-256 of
+# csrc/gemm.hip at the time, and a different source reports null.
+TRAFFIC = {
+    # FETCH_SIZE 528878.5 KiB x 2.0 + WRITE_SIZE 49153.0 KiB x 1.0 per launch; the 1 GiB
+    # copy read 524301 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE.
+    "qwen3_bf16": {"gemm_src": "1e1b858900b7c2f4fc04a2e206446082325d9d39101e8d801662d6b588cf387d",
+                   "bytes": 1133475840},
+}
+
+
+def gemm_source_digest() -> str:
+    path = os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", "gemm.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload: str):
+    rec = TRAFFIC.get(workload)
+    if rec is None or rec["gemm_src"] != gemm_source_digest():
+        return None
+    return rec["bytes"]
+
+
+def copy_calibration():
+    """1 GiB bf16 device-to-device copy, five times: 1 GiB read and 1 GiB written each."""
+    n = 1 << 29
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "copies": 5}),
+          flush=True)
 
 
 def log(*a):
@@ -70,6 +111,21 @@ def run_layer(cfg, d, fcfg, ws, out, shared_out):
                       out=out, shared_out=shared_out, workspace=ws)
 
 
+def time_launches(call, reps: int, stream) -> float:
+    """Average duration in ms of one call, HIP events recorded around each launch on the
+    stream the kernels run on."""
+    for _ in range(3):
+        call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
 def time_gate_up(cfg, d, reps: int):
     """Average duration of one grouped gate_up GEMM launch, HIP events on its stream."""
     stream = torch.cuda.current_stream()
@@ -81,17 +137,7 @@ def time_gate_up(cfg, d, reps: int):
     call = lambda: B.moe_grouped_gemm_swiglu(d["hidden"], d["w_gate_up"], off, cfg.act,
                                              d.get("b_gate_up"), a_rows=srt,
                                              a_rows_div=cfg.K, out=act, stream=stream)
-    for _ in range(3):
-        call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
-        a.record(stream)
-        call()
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = [a.elapsed_time(b) for a, b in evs]
-    return float(np.mean(ms)), distinct_experts(ids)
+    return time_launches(call, reps, stream), distinct_experts(ids)
 
 
 def cpu_baseline(cfg, d, budget_s: float):
@@ -142,11 +188,15 @@ def main():
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the path is built and measured on a single "
               "MI355X (no collectives); use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     cfg = I.CONFIGS[args.workload]
     if cfg.H == 0:
         sys.exit("router-only workload: not a bench line")
@@ -171,11 +221,30 @@ def main():
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
 
-    log("[bench] timing the gate_up kernel")
-    k_ms, n_exp = time_gate_up(cfg, d, args.kernel_reps)
-    k_bytes = gate_up_algorithmic_bytes(cfg, n_exp)
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    _, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize,
+                                                        cfg.rsf, cfg.G, cfg.TG),
+                               d.get("correction_bias"), d.get("expert_ids"))
+    n_exp = distinct_experts(ids)
     l_bytes, l_flops = layer_algorithmic(cfg, n_exp)
+    if backend == "staged":
+        # the grouped gate_up GEMM with its fused activation dominates the layer
+        log("[bench] timing the gate_up kernel")
+        k_ms, _ = time_gate_up(cfg, d, args.kernel_reps)
+        k_bytes = gate_up_algorithmic_bytes(cfg, n_exp)
+        k_name = "gemm_bf16_kernel (grouped gate_up + SwiGLU)"
+        k_traffic = recorded_traffic(cfg.name)
+    else:
+        # decode: the two indexed kernels stream the touched experts' weights; the
+        # roofline entry covers one whole layer launch (route, permute, both indexed
+        # kernels, combine) against the layer's minimum bytes
+        log("[bench] timing the indexed layer")
+        stream = torch.cuda.current_stream()
+        k_ms = time_launches(lambda: run_layer(cfg, d, fcfg, ws, out, shared_out),
+                             args.kernel_reps, stream)
+        k_bytes = l_bytes
+        k_name = "moe_ffn_forward, indexed backend (indexed_kernel gate_up + down dominate)"
+        k_traffic = None
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -193,9 +262,10 @@ def main():
                    "top_k": cfg.K, "scoring": cfg.scoring, "activation": cfg.act,
                    "num_expert_group": cfg.G, "topk_group": cfg.TG, "F_shared": cfg.F_s,
                    "backend": backend, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "gemm_bf16_kernel (grouped gate_up + SwiGLU)",
+        "roofline": {"bound": "hbm", "kernel": k_name,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": k_traffic,
                      "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes},
         "layer": {"hbm_frac": round(l_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(l_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),

@@ -41,14 +41,16 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 64, LDK = BK + 8;      // K step; LDS row stride in elements
-constexpr int NT = 256;
 constexpr int kMaxE = 1024;
 constexpr int kXcd = 8;
 // Tile shape: RB 32-row blocks of token rows and CB 32-row blocks of weight rows per wave;
-// waves (wm, wn) are 2 x 2, so a tile holds 64*RB token rows and 64*CB weight rows.
-template <int RB, int CB> constexpr int stage_elems() { return (64 * RB + 64 * CB) * LDK; }
-template <int RB, int CB> constexpr size_t lds_bytes() { return (size_t)2 * stage_elems<RB, CB>() * 2; }
+// waves (wm, wn) are WM x WN, so a tile holds 32*RB*WM token rows and 32*CB*WN weight rows.
+// BK = K step; LDS rows are BK + 8 elements apart (16-byte fragment reads conflict-free).
+template <int RB, int CB, int BK, int NT, int WM> constexpr int stage_elems() {
+  return (32 * RB * WM + 32 * CB * (NT / 64 / WM)) * (BK + 8);
+}
+template <int RB, int CB, int BK, int NT, int WM, int NBUF>
+constexpr size_t lds_bytes() { return (size_t)NBUF * stage_elems<RB, CB, BK, NT, WM>() * 2; }
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
 
 __device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float beta,
@@ -69,6 +71,7 @@ __device__ __forceinline__ int rows_per_tile(int rows, int bm) {
 
 // Builds s_pre[0..E] = exclusive prefix of per-expert tile counts and copies the offsets
 // into s_off. offsets == NULL means one expert that owns rows 0 .. M-1. All NT threads.
+template <int NT>
 __device__ void build_tile_map(const int32_t* offsets, int E, int M, int bm, int* s_off,
                                int* s_pre, int* s_tmp) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -115,12 +118,18 @@ __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t 
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-template <int RB, int CB, int PA, bool ACT, int LAYOUT, bool OUT_F32>
-__global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int BMX = 64 * RB, BNW = 64 * CB;
+template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
+          int LAYOUT, bool OUT_F32>
+__global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
+  constexpr int LDK = BK + 8, CPR = BK / 8, RSTEP = NT / CPR;  // 16-byte pieces per row
+  constexpr int WN = NT / 64 / WM;  // waves: WM along the token rows x WN along the weights
+  constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * WN;
   constexpr int NLD = (BMX * BK / 8) / NT, NLDB = (BNW * BK / 8) / NT;
-  constexpr int kStageElems = stage_elems<RB, CB>();
-  static_assert(lds_bytes<RB, CB>() >= 2 * (kMaxE + 1) * sizeof(int), "tile map alias");
+  constexpr int kStageElems = stage_elems<RB, CB, BK, NT, WM>();
+  static_assert(lds_bytes<RB, CB, BK, NT, WM, NBUF>() >= 2 * (kMaxE + 1) * sizeof(int),
+                "tile map alias");
+  static_assert(NBUF == 2 || PA == 1, "one LDS buffer goes with A one step ahead");
+  static_assert(NBUF == 2 || MID >= BK / 16, "one LDS buffer: the store follows the last MFMA");
   static_assert(CB == 2 || CB == 4, "weight blocks per wave");
   __shared__ int s_tmp[NT / 64];
   extern __shared__ __align__(16) uint16_t smem[];  // [2][BMX + BNW][LDK]
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = g.E;
-  build_tile_map(g.offsets, E, g.M, BMX, s_off, s_pre, s_tmp);
+  build_tile_map<NT>(g.offsets, E, g.M, BMX, s_off, s_pre, s_tmp);
 
   const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
   const int n_valid = s_pre[E] * n_tiles_n;
@@ -152,9 +161,9 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
   const int Kd = g.Kd;
   __syncthreads();  // every thread has read the map; the buffers become stages
 
-  // ---- loads: thread tid moves 16-byte piece (tid & 7) of rows (tid >> 3) + 32 i, i < NLD,
-  // of both the A and the B tile (8 consecutive lanes read one 128-byte row segment).
-  const int kc = (tid & 7) * 8;
+  // ---- loads: thread tid moves 16-byte piece tid % CPR of rows tid / CPR + RSTEP i, i < NLD,
+  // of both the A and the B tile (CPR consecutive lanes read one row segment).
+  const int kc = (tid % CPR) * 8;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, 0x7fffffff, 0x00020000);
   const uint16_t* Bexp = (const uint16_t*)g.b + (int64_t)e * g.Nw * Kd;
@@ -163,7 +172,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
   uint32_t aoff[NLD], boff[NLDB];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = tid / CPR + RSTEP * i;
     const bool aon = r < rows;
     const int m = m0 + (aon ? r : 0);
     const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
   }
 #pragma unroll
   for (int i = 0; i < NLDB; ++i) {
-    const int r = (tid >> 3) + 32 * i;
+    const int r = tid / CPR + RSTEP * i;
     int wr;
     bool bon;
     if (ACT) {
@@ -203,15 +212,15 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
     uint16_t* la = smem + buf * kStageElems;
     uint16_t* lb = la + BMX * LDK;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) *(bf16x8*)(la + ((tid >> 3) + 32 * i) * LDK + kc) = xa[i];
+    for (int i = 0; i < NLD; ++i) *(bf16x8*)(la + (tid / CPR + RSTEP * i) * LDK + kc) = xa[i];
 #pragma unroll
-    for (int i = 0; i < NLDB; ++i) *(bf16x8*)(lb + ((tid >> 3) + 32 * i) * LDK + kc) = xb[i];
+    for (int i = 0; i < NLDB; ++i) *(bf16x8*)(lb + (tid / CPR + RSTEP * i) * LDK + kc) = xb[i];
   };
 
-  // wave (wm, wn): row blocks wm, wm+2, ... (RB of them); weight rows: for the gated activation
-  // gate rows wn*16*CB + [0,16*CB) and the matching up rows BNW/2 + the same; else
-  // wn*32*CB + [0,32*CB).
-  const int wm = wave & 1, wn = wave >> 1;
+  // wave (wm, wn): row blocks wm, wm+WM, ... (RB of them); weight rows: for the gated
+  // activation gate rows wn*16*CB + [0,16*CB) and the matching up rows BNW/2 + the same;
+  // else wn*32*CB + [0,32*CB).
+  const int wm = wave % WM, wn = wave / WM;
   int brow[CB];
 #pragma unroll
   for (int j = 0; j < CB; ++j)
@@ -219,7 +228,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
                    : (wn * 32 * CB + j * 32)) +
               (lane & 31);
   const int kq = (lane >> 5) * 8;
-  const int nbw = (nb - wm + 1) / 2;  // live row blocks of this wave
+  const int nbw = nb > wm ? (nb - wm + WM - 1) / WM : 0;  // live row blocks of this wave
 
   f32x16 acc[RB][CB];
 #pragma unroll
@@ -231,24 +240,35 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
   // of a sub-step is issued before its MFMAs.
   auto main_loop = [&](auto nbw_c) {
     constexpr int NBW = decltype(nbw_c)::value;
-    auto compute = [&](int buf) {
+    // compute(buf, mid): the MFMAs of one K step from LDS buffer buf; mid() (the store of
+    // the next step and the loads two steps ahead) runs after sub-step MID - 1, pinned
+    // there, so those waits and LDS writes overlap the remaining MFMAs (MID = BK/16: at
+    // the end).
+    auto compute = [&](int buf, auto&& mid) {
       const uint16_t* sa = smem + buf * kStageElems;
       const uint16_t* sb = sa + BMX * LDK;
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
+        if (ks == MID) {
+          __builtin_amdgcn_sched_barrier(0);
+          mid();
+          __builtin_amdgcn_sched_barrier(0);
+        }
         bf16x8 fb[CB], fa[NBW];
 #pragma unroll
         for (int j = 0; j < CB; ++j) fb[j] = *(const bf16x8*)(sb + brow[j] * LDK + ks * 16 + kq);
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
-          fa[i] = *(const bf16x8*)(sa + ((wm + 2 * i) * 32 + (lane & 31)) * LDK + ks * 16 + kq);
+          fa[i] = *(const bf16x8*)(sa + ((wm + WM * i) * 32 + (lane & 31)) * LDK + ks * 16 + kq);
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
 #pragma unroll
           for (int j = 0; j < CB; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
       }
+      if (MID >= BK / 16) mid();
     };
+    auto none = [] {};
     // Step s uses LDS buffer s % 2 and weight set sb[s % 2] (and, with PA = 2, A set
     // sa[s % 2]). After storing step k+1 the loads of the steps two ahead (PA = 2: A and
     // weights of k+3) or A of k+2 and then the weights of k+3 (PA = 1) are issued, so the
@@ -267,18 +287,23 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
       load_b(2 * BK, sb0);
       __syncthreads();
       for (; k + 1 < nk; k += 2) {
-        compute(0);
-        store_stage(1, sa1, sb1);
-        load_a((k + 3) * BK, sa1);
-        load_b((k + 3) * BK, sb1);
+        compute(0, [&] {
+          store_stage(1, sa1, sb1);
+          load_a((k + 3) * BK, sa1);
+          load_b((k + 3) * BK, sb1);
+        });
         __syncthreads();
-        compute(1);
-        store_stage(0, sa0, sb0);
-        load_a((k + 4) * BK, sa0);
-        load_b((k + 4) * BK, sb0);
+        compute(1, [&] {
+          store_stage(0, sa0, sb0);
+          load_a((k + 4) * BK, sa0);
+          load_b((k + 4) * BK, sb0);
+        });
         __syncthreads();
       }
     } else {
+      // With one LDS buffer (NBUF == 1) every step ends with a barrier before the store
+      // that overwrites it, and a barrier after.
+      constexpr int B1 = NBUF == 2 ? 1 : 0;
       load_a(0, sa0);
       load_b(0, sb0);
       load_b(BK, sb1);
@@ -287,19 +312,23 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
       load_b(2 * BK, sb0);
       __syncthreads();
       for (; k + 1 < nk; k += 2) {
-        compute(0);
-        store_stage(1, sa0, sb1);
-        load_a((k + 2) * BK, sa0);
-        load_b((k + 3) * BK, sb1);
+        compute(0, [&] {
+          if (NBUF == 1) __syncthreads();
+          store_stage(B1, sa0, sb1);
+          load_a((k + 2) * BK, sa0);
+          load_b((k + 3) * BK, sb1);
+        });
         __syncthreads();
-        compute(1);
-        store_stage(0, sa0, sb0);
-        load_a((k + 3) * BK, sa0);
-        load_b((k + 4) * BK, sb0);
+        compute(B1, [&] {
+          if (NBUF == 1) __syncthreads();
+          store_stage(0, sa0, sb0);
+          load_a((k + 3) * BK, sa0);
+          load_b((k + 4) * BK, sb0);
+        });
         __syncthreads();
       }
     }
-    if (k < nk) compute(0);  // odd number of K steps: the last one is in buffer 0
+    if (k < nk) compute(0, none);  // odd number of K steps: the last one is in buffer 0
   };
   // With 128-row tiles the loop is compiled for 2 and for 1 live row blocks of the wave;
   // with 256-row tiles one loop covers all 4 (blocks past the tile's last row read rows
@@ -307,6 +336,9 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
   if constexpr (RB == 2) {
     if (nbw >= 2) main_loop(std::integral_constant<int, 2>{});
     else main_loop(std::integral_constant<int, 1>{});
+  } else if constexpr (RB == 4 && CB == 2) {
+    if (nbw >= 3) main_loop(std::integral_constant<int, 4>{});
+    else main_loop(std::integral_constant<int, 2>{});
   } else {
     main_loop(std::integral_constant<int, RB>{});
   }
@@ -328,7 +360,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           if (i < nbw) {
-            const int rb = wm + 2 * i;
+            const int rb = wm + WM * i;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -352,7 +384,7 @@ __global__ __launch_bounds__(NT, CB == 2 ? 2 : 1) void gemm_bf16_kernel(GemmArgs
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           if (i < nbw) {
-            const int rb = wm + 2 * i;
+            const int rb = wm + WM * i;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -414,28 +446,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-template <int RB, int CB, int PA, bool ACT, int LAYOUT, bool OUT_F32>
+template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
+          int LAYOUT, bool OUT_F32>
 hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
-  constexpr int BMX = 64 * RB, BNW = 64 * CB;
+  constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * (NT / 64 / WM);
   const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
   const int64_t max_tiles = (g.M + BMX - 1) / BMX + (g.E < g.M ? g.E : g.M);
   int64_t grid = max_tiles * n_tiles_n;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  const auto kern = gemm_bf16_kernel<RB, CB, PA, ACT, LAYOUT, OUT_F32>;
+  const auto kern = gemm_bf16_kernel<RB, CB, PA, BK, NT, WM, OCC, MID, NBUF, ACT, LAYOUT, OUT_F32>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes<RB, CB>());
+                                       (int)lds_bytes<RB, CB, BK, NT, WM, NBUF>());
   if (err != hipSuccess) return err;
-  kern<<<dim3((unsigned)grid), dim3(NT), lds_bytes<RB, CB>(), s>>>(g);
+  kern<<<dim3((unsigned)grid), dim3(NT), lds_bytes<RB, CB, BK, NT, WM, NBUF>(), s>>>(g);
   return hipGetLastError();
 }
 
-// 128 x 128 tiles, two workgroups per CU, token rows and weights both two K steps ahead:
-// of the shapes this kernel is written for (also 128 x 256 and 256 x 256 with one
-// workgroup per CU, and A one step ahead) the fastest on every workload measured.
+// 128 x 128 tiles, two workgroups per CU, token rows and weights both two K steps ahead.
+// Of the shapes the kernel is written for (also 128 x 256 and 256 x 256 with eight waves,
+// A one step ahead, one LDS buffer) this one measured fastest or within 2% of the fastest
+// on every workload tried.
 template <bool ACT, int LAYOUT, bool OUT_F32>
 hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
-  return launch_bf16_shape<2, 2, 2, ACT, LAYOUT, OUT_F32>(g, s);
+  // <RB, CB, PA, BK, NT, WM, OCC, MID, NBUF>
+  return launch_bf16_shape<2, 2, 2, 64, 256, 2, 2, 4, 2, ACT, LAYOUT, OUT_F32>(g, s);
 }
 
 }  // namespace

@@ -5,12 +5,23 @@
 //      picks this backend when T*K <= 2E with silu_and_mul, no bias, H % 128 == 0 and
 //      F % 256 == 0 (those are the widths these kernels are tiled for).
 //
-// Work items are (distinct expert, 64-row slice of its weights). A wave owns 16 weight
-// rows (for gate_up: 16 gate rows and the 16 matching up rows) and streams them over
-// the full contraction straight from HBM into v_mfma_f32_16x16x32_bf16 operands, with
-// the expert's routes (at most 16 per pass) as the other operand. The order of the
-// contraction inside a 128-wide block is permuted (both operands alike, so the sum is
-// unchanged) so that each lane reads 64 contiguous bytes of a row per block.
+// With a handful of routes per expert the work is a stream of the touched experts'
+// weights, so the kernels are built around reading weight rows at full HBM rate:
+//   * A wave owns 32 weight rows (gate_up: 16 gate rows and the 16 matching up rows;
+//     down: 32 rows of W_d) and streams them over the whole contraction in 256-byte
+//     blocks. Each load instruction reads 4 rows x 256 contiguous bytes (16 lanes per
+//     row), whole cache lines, the pattern that streams at full rate.
+//   * MFMA operands need the opposite layout (a lane holds 8 contraction elements of ONE
+//     row), so each block goes through a wave-private LDS tile: the wave writes the
+//     block as loaded and reads it back in v_mfma_f32_16x16x32_bf16 operand order. The
+//     16-byte slots are XOR-swizzled with the row so both directions are conflict-free.
+//     No workgroup barrier is involved; LDS operations of one wave complete in order.
+//   * Three blocks of loads are in flight per wave (register sets rotated by an unrolled
+//     loop); the expert's routes (16 per pass) are the other MFMA operand, read straight
+//     from the token rows (gate_up) or the activation rows (down).
+// Inside a block the contraction order is permuted identically for both operands
+// (MFMA u, lane quarter q takes the 8 elements of piece 4u + q), so the sums are those
+// of the plain dot products up to float32 rounding order.
 //   gate_up: act[route, j] = silu(h W_g[j]) * (h W_u[j]), rounded to bf16 (workspace)
 //   down:    y[route, n]   = act[route] . W_d[n], float32 (workspace); the combine
 //            kernel then sums the routes of each token.
@@ -19,130 +30,142 @@
 namespace moe {
 namespace {
 
-constexpr int kRowsPerWave = 16;
-constexpr int kWaves = 4;
-constexpr int kRowsPerBlock = kRowsPerWave * kWaves;  // 64
-constexpr int kKBlock = 128;
-constexpr int kUnroll = 2;  // 128-wide blocks in flight per lane
+constexpr int kWaves = 4;       // waves per workgroup, each with its own work item
+constexpr int kBlk = 128;       // contraction elements per block (256 bytes of a row)
+constexpr int kSets = 3;        // blocks in flight per wave
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
 
-// One 128-wide contraction block: lane (row l%16, quarter q = l/16) holds the 32
-// consecutive elements [q*32, q*32+32) as four 8-element pieces; piece u feeds MFMA u.
-struct Frag {
-  bf16x8 p[4];
-};
-
-__device__ __forceinline__ Frag load_frag(const uint16_t* row_block_base, int q) {
-  Frag f;
-  const bf16x8* src = (const bf16x8*)(row_block_base + q * 32);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) f.p[u] = __builtin_nontemporal_load(src + u);
-  return f;
-}
-
-__device__ __forceinline__ Frag load_frag_cached(const uint16_t* row_block_base, int q) {
-  Frag f;
-  const bf16x8* src = (const bf16x8*)(row_block_base + q * 32);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) f.p[u] = src[u];
-  return f;
+__device__ __forceinline__ bf16x8 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * (1.0f / (1.0f + __expf(-g))) * u;
 }
 
-// gate_up: grid.x = max distinct experts, grid.y = F / 64.
-__global__ __launch_bounds__(64 * kWaves) void indexed_gate_up_kernel(IndexedArgs p) {
-  const int n_active = p.active[p.E];
-  if ((int)blockIdx.x >= n_active) return;
-  const int e = p.active[blockIdx.x];
-  const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, q = lane >> 4;
-  const int j = blockIdx.y * kRowsPerBlock + wave * kRowsPerWave + row;  // act column
-  const int H = p.H, F = p.F;
-  const uint16_t* wg = p.w_gate_up + ((int64_t)e * 2 * F + j) * H;
-  const uint16_t* wu = p.w_gate_up + ((int64_t)e * 2 * F + F + j) * H;
+// One wave: rows row_g[0] + [0,16) and row_g[1] + [0,16) of the expert's weight matrix
+// w (rows of Kd elements) against the routes [c0, c0 + 16) of the expert, over the full
+// contraction. acc[g] receives D[i][c] (lane: route c = lane % 16, rows 4*(lane/16)+r).
+template <bool GATE_UP>
+__device__ __forceinline__ void stream_rows(const IndexedArgs& p, bf16x8 (*stage)[16],
+                                            __amdgpu_buffer_rsrc_t rw, const int* row_g,
+                                            int Kd, int c0, int o1, f32x4* acc) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane >> 4, piece = lane & 15;  // load layout: row 4u + lr, 16-byte piece
+  const int fr = lane & 15, fq = lane >> 4;     // MFMA layout: row / route fr, quarter fq
+  // Weight offsets of this lane's 8 loads per block (group g, load u).
+  uint32_t woff[8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      woff[g * 4 + u] = ((uint32_t)(row_g[g] + 4 * u + lr) * (uint32_t)Kd + piece * 8) * 2u;
+  // Route operand: the row of route slot c0 + fr (token row for gate_up, permuted
+  // activation row for down); pieces 4u + fq of each block.
+  const int slot = c0 + fr;
+  const bool has = slot < o1;
+  const int src = has ? (GATE_UP ? p.sorted_route[slot] / p.K : slot) : 0;
+  const void* xbase = GATE_UP ? (const void*)p.hidden : (const void*)p.act;
+  const int xrows = GATE_UP ? p.T : p.T * p.K;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xbase, (short)0, (int)((int64_t)xrows * Kd * 2), 0x00020000);
+  uint32_t xoff[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    xoff[u] = has ? ((uint32_t)src * (uint32_t)Kd + (4 * u + fq) * 8) * 2u : kOOB;
 
-  for (int c0 = o0; c0 < o1; c0 += 16) {
-    const int slot = c0 + row;  // route slot this lane feeds on the B side
-    const bool has = slot < o1;
-    const uint16_t* xr = p.hidden + (int64_t)(has ? p.sorted_route[slot] / p.K : 0) * H;
-    f32x4 ag = {0, 0, 0, 0}, au = {0, 0, 0, 0};
-    for (int k0 = 0; k0 < H; k0 += kKBlock * kUnroll) {
-      Frag fg[kUnroll], fu[kUnroll], fx[kUnroll];
+  const int nb = Kd / kBlk;
+  bf16x8 w0[8], w1[8], w2[8], x0[4], x1[4], x2[4];
+  auto issue = [&](int b, bf16x8* w, bf16x8* x) {
+    const bool in = b < nb;
+    const uint32_t kb = (uint32_t)b * (kBlk * 2);
 #pragma unroll
-      for (int b = 0; b < kUnroll; ++b) {
-        const int kb = k0 + b * kKBlock;
-        const bool in = kb < H;  // H % 128 == 0; the last pair may be half empty
-        for (int u = 0; u < 4; ++u) fg[b].p[u] = fu[b].p[u] = fx[b].p[u] = bf16x8{};
-        if (in) {
-          fg[b] = load_frag(wg + kb, q);
-          fu[b] = load_frag(wu + kb, q);
-          if (has) fx[b] = load_frag_cached(xr + kb, q);
-        }
+    for (int i = 0; i < 8; ++i) w[i] = ld16(rw, in ? woff[i] + kb : kOOB);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = ld16(rx, in ? xoff[u] + kb : kOOB);
+  };
+  auto step = [&](const bf16x8* w, const bf16x8* x) {
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * u + lr;
+        stage[g * 16 + r][piece ^ r] = w[g * 4 + u];
       }
+    __builtin_amdgcn_wave_barrier();
+    bf16x8 f[2][4];
 #pragma unroll
-      for (int b = 0; b < kUnroll; ++b)
+    for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ag = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fg[b].p[u], fx[b].p[u], ag, 0, 0, 0);
-          au = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fu[b].p[u], fx[b].p[u], au, 0, 0, 0);
-        }
-    }
-    // D[i][s]: lane holds route slot s = lane%16 and weight rows i = 4*(lane/16) + r.
-    const int s = c0 + (lane & 15);
-    if (s < o1) {
+      for (int u = 0; u < 4; ++u) f[g][u] = stage[g * 16 + fr][(4 * u + fq) ^ fr];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int jj = blockIdx.y * kRowsPerBlock + wave * kRowsPerWave + 4 * q + r;
-        p.act[(int64_t)s * F + jj] = f32_to_bf16(silu_mul(ag[r], au[r]));
-      }
-    }
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[g][u], x[u], acc[g], 0, 0, 0);
+  };
+
+  issue(0, w0, x0);
+  issue(1, w1, x1);
+  issue(2, w2, x2);
+  int b = 0;
+  for (; b + kSets <= nb; b += kSets) {
+    step(w0, x0);
+    issue(b + 3, w0, x0);
+    step(w1, x1);
+    issue(b + 4, w1, x1);
+    step(w2, x2);
+    issue(b + 5, w2, x2);
   }
+  if (b < nb) step(w0, x0);
+  if (b + 1 < nb) step(w1, x1);
 }
 
-// down: grid.x = max distinct experts, grid.y = H / 64.
-__global__ __launch_bounds__(64 * kWaves) void indexed_down_kernel(IndexedArgs p) {
+// Work items per expert: gate_up F/16 (16 act columns each), down H/32 (32 hidden rows);
+// each workgroup takes kWaves consecutive items of one expert.
+template <bool GATE_UP>
+__global__ __launch_bounds__(64 * kWaves, 2) void indexed_kernel(IndexedArgs p) {
+  __shared__ bf16x8 stage_all[kWaves][32][16];
+  const int items = GATE_UP ? p.F / 16 : p.H / 32;
+  const int wg_per_e = items / kWaves;
+  const int a = blockIdx.x / wg_per_e;
   const int n_active = p.active[p.E];
-  if ((int)blockIdx.x >= n_active) return;
-  const int e = p.active[blockIdx.x];
+  if (a >= n_active) return;  // uniform per workgroup
+  const int e = p.active[a];
   const int o0 = p.offsets[e], o1 = p.offsets[e + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, q = lane >> 4;
-  const int n = blockIdx.y * kRowsPerBlock + wave * kRowsPerWave + row;  // hidden index
+  const int item = (blockIdx.x % wg_per_e) * kWaves + wave;
   const int H = p.H, F = p.F;
-  const uint16_t* wd = p.w_down + ((int64_t)e * H + n) * F;
-
+  const int Kd = GATE_UP ? H : F;
+  const uint16_t* wexp = GATE_UP ? p.w_gate_up + (int64_t)e * 2 * F * H
+                                 : p.w_down + (int64_t)e * H * F;
+  const int nrows = GATE_UP ? 2 * F : H;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wexp, (short)0, (int)((int64_t)nrows * Kd * 2), 0x00020000);
+  int row_g[2];
+  if (GATE_UP) {
+    row_g[0] = item * 16;      // gate rows j0 .. j0+15
+    row_g[1] = F + item * 16;  // the matching up rows
+  } else {
+    row_g[0] = item * 32;
+    row_g[1] = item * 32 + 16;
+  }
+  const int c = lane & 15, q = lane >> 4;
   for (int c0 = o0; c0 < o1; c0 += 16) {
-    const int slot = c0 + row;
-    const bool has = slot < o1;
-    const uint16_t* ar = p.act + (int64_t)(has ? slot : 0) * F;
-    f32x4 acc = {0, 0, 0, 0};
-    for (int k0 = 0; k0 < F; k0 += kKBlock * kUnroll) {
-      Frag fw[kUnroll], fa[kUnroll];
-#pragma unroll
-      for (int b = 0; b < kUnroll; ++b) {
-        const int kb = k0 + b * kKBlock;
-        const bool in = kb < F;
-        for (int u = 0; u < 4; ++u) fw[b].p[u] = fa[b].p[u] = bf16x8{};
-        if (in) {
-          fw[b] = load_frag(wd + kb, q);
-          if (has) fa[b] = load_frag_cached(ar + kb, q);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kUnroll; ++b)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[b].p[u], fa[b].p[u], acc, 0, 0, 0);
-    }
-    const int s = c0 + (lane & 15);
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    stream_rows<GATE_UP>(p, stage_all[wave], rw, row_g, Kd, c0, o1, acc);
+    const int s = c0 + c;
     if (s < o1) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int nn = blockIdx.y * kRowsPerBlock + wave * kRowsPerWave + 4 * q + r;
-        p.y[(int64_t)s * H + nn] = acc[r];
+        const int i = 4 * q + r;
+        if (GATE_UP)
+          p.act[(int64_t)s * F + item * 16 + i] = f32_to_bf16(silu_mul(acc[0][r], acc[1][r]));
+        else {
+          p.y[(int64_t)s * H + item * 32 + i] = acc[0][r];
+          p.y[(int64_t)s * H + item * 32 + 16 + i] = acc[1][r];
+        }
       }
     }
   }
@@ -154,10 +177,10 @@ hipError_t launch_indexed_mlp(const IndexedArgs& a, hipStream_t s) {
   const int R = a.T * a.K;
   const int max_active = R < a.E ? R : a.E;
   if (max_active <= 0) return hipSuccess;
-  indexed_gate_up_kernel<<<dim3(max_active, a.F / kRowsPerBlock), 64 * kWaves, 0, s>>>(a);
+  indexed_kernel<true><<<dim3(max_active * (a.F / 16 / kWaves)), 64 * kWaves, 0, s>>>(a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  indexed_down_kernel<<<dim3(max_active, a.H / kRowsPerBlock), 64 * kWaves, 0, s>>>(a);
+  indexed_kernel<false><<<dim3(max_active * (a.H / 32 / kWaves)), 64 * kWaves, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -92,6 +92,23 @@ def test_ffn_small(name):
         assert_close(np64(out_s), np64(out), "bf16", "indexed vs staged")
 
 
+def test_indexed_passes_over_route_groups():
+    """One expert takes every route (40 > 16), so the decode backend runs three passes of
+    16, 16 and 8 routes over that expert's weights."""
+    cfg = SMALL["decode_many_routes_per_expert"]
+    say("[ffn] indexed, 40 routes on one expert")
+    d = I.make_inputs(cfg, device="cuda")
+    d["logits"][:, 3] += 30.0
+    assert B.moe_ffn_backend(B.ffn_cfg(cfg), False) == 2
+    out, shared = run_gpu(cfg, d)
+    torch.cuda.synchronize()
+    r = compare(cfg, d, out, shared, np.arange(cfg.T), "indexed 40 routes")
+    assert (np.asarray(r.topk_ids) == 3).all()
+    out_s, _ = run_gpu(cfg, d, "staged")
+    torch.cuda.synchronize()
+    assert_close(np64(out_s), np64(out), "bf16", "indexed vs staged")
+
+
 def test_ffn_deterministic():
     cfg = SMALL["dsv3_like"]
     d = I.make_inputs(cfg, device="cuda")
