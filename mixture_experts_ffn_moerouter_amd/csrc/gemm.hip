@@ -11,12 +11,12 @@
 //      limit <= 0 disables both clamps.
 //
 // bf16 kernel, templated on the tile shape: RB and CB 32-row blocks of token rows and of
-// weight rows per wave, waves arranged 2 x 2, so a tile is 64*RB token rows x 64*CB weight
-// rows, K in steps of 64 (v_mfma_f32_32x32x16_bf16, float32 accumulators). The shape in
-// use is 128 x 128 with two workgroups (eight waves) per CU. Weight streaming from HBM
-// bounds these shapes, so the loop keeps the loads of the next two K steps in flight in
-// registers (token rows PA steps ahead, weights two) while the matrix cores work on the
-// step held in LDS; LDS is double buffered (row stride 72 elements: conflict-free 16-byte
+// weight rows per wave, waves arranged WM x WN, so a tile is 32*RB*WM token rows x
+// 32*CB*WN weight rows, K in steps of 64 (v_mfma_f32_32x32x16_bf16, float32
+// accumulators); 128 x 128 and 128 x 256 are in use (see launch_bf16). The loop keeps
+// the loads of the next K steps in flight in registers (token rows PA steps ahead,
+// weights two) while the matrix cores work on the step held in LDS; LDS is double
+// buffered (row stride 72 elements: conflict-free 16-byte
 // fragment reads), and each load instruction reads whole 128-byte row segments. For the
 // gated activation the tile's weight rows are gate rows and the matching up rows, placed
 // so that a lane's gate and up accumulators hold the same output element; the epilogue
@@ -463,13 +463,18 @@ hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 128 x 128 tiles, two workgroups per CU, token rows and weights both two K steps ahead.
-// Of the shapes the kernel is written for (also 128 x 256 and 256 x 256 with eight waves,
-// A one step ahead, one LDS buffer) this one measured fastest or within 2% of the fastest
-// on every workload tried.
+// Two shapes, chosen by the contraction length. Long contractions (Kd >= 2560) take 128
+// token rows x 256 weight rows per workgroup, eight waves (2 x 4) of 64 x 64, one
+// workgroup per CU: half as many n-tiles re-read each expert's token rows per weight
+// byte. Shorter ones take 128 x 128 with four waves and two workgroups per CU, where one
+// workgroup's prologue and epilogue overlap the other's K loop. Both keep the two
+// operands two K steps ahead. Measured in one process, alternating the shapes: 5% and 3%
+// faster layers with the wide tile at Kd 7168 and 2880, 2% slower at Kd 2048 / 768.
 template <bool ACT, int LAYOUT, bool OUT_F32>
 hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
   // <RB, CB, PA, BK, NT, WM, OCC, MID, NBUF>
+  if (g.Kd >= 2560)
+    return launch_bf16_shape<2, 2, 2, 64, 512, 2, 1, 4, 2, ACT, LAYOUT, OUT_F32>(g, s);
   return launch_bf16_shape<2, 2, 2, 64, 256, 2, 2, 4, 2, ACT, LAYOUT, OUT_F32>(g, s);
 }
 

@@ -26,7 +26,8 @@ SEGMENTS = {
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 @pytest.mark.parametrize("seg", sorted(SEGMENTS))
-@pytest.mark.parametrize("shape", [(256, 384), (200, 136), (72, 40)])  # (K, N)
+# (K, N); K >= 2560 takes the wide 128 x 256 tile, with a ragged K tail here
+@pytest.mark.parametrize("shape", [(256, 384), (200, 136), (72, 40), (2600, 300)])
 @pytest.mark.parametrize("bias", [False, True])
 def test_grouped_gemm(dt, seg, shape, bias):
     Kd, N = shape
@@ -59,11 +60,14 @@ ACTS = {"silu_and_mul": "silu_and_mul", "swigluoai": "swigluoai",
 @pytest.mark.parametrize("seg", ["ragged", "uniform256"])
 @pytest.mark.parametrize("act", sorted(ACTS))
 @pytest.mark.parametrize("gather", [False, True])
-def test_grouped_gemm_swiglu(dt, seg, act, gather):
+@pytest.mark.parametrize("H", [200, 2600])
+def test_grouped_gemm_swiglu(dt, seg, act, gather, H):
     sizes = SEGMENTS[seg]
     E, M = len(sizes), int(sum(sizes))
-    H, F = 200, 96  # ragged K tile (200 = 3*64 + 8) and ragged act tile (96 = 64 + 32)
-    say(f"[gemm-act] dt={dt} seg={seg} act={act} gather={gather}")
+    # ragged K tiles (200 = 3*64 + 8, 2600 = 40*64 + 40; 2600 takes the wide tile) and a
+    # ragged activation tile (96 = 64 + 32)
+    F = 96
+    say(f"[gemm-act] dt={dt} seg={seg} act={act} gather={gather} H={H}")
     g = torch.Generator(device="cuda").manual_seed(2)
     T = max(1, M // 3 + 1)
     src = (3.0 * torch.randn((T if gather else M, H), device="cuda", generator=g)).to(DT[dt])
