@@ -37,10 +37,10 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # figure belongs to the kernel source it was measured on: gemm_src is the SHA-256 of
 # csrc/gemm.hip at the time, and a different source reports null.
 TRAFFIC = {
-    # FETCH_SIZE 528878.5 KiB x 2.0 + WRITE_SIZE 49153.0 KiB x 1.0 per launch; the 1 GiB
-    # copy read 524301 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE.
-    "qwen3_bf16": {"gemm_src": "1e1b858900b7c2f4fc04a2e206446082325d9d39101e8d801662d6b588cf387d",
-                   "bytes": 1133475840},
+    # FETCH_SIZE 529162.9 KiB x 1.99995 + WRITE_SIZE 49153.0 KiB x 1.0 per launch; the 1 GiB
+    # copy read 524301.3 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE.
+    "qwen3_bf16": {"gemm_src": "7349f9934277d1db207905bedca1cca4d1fc235a9567ff401c2f8b8a27913ccf",
+                   "bytes": 1134030807},
 }
 
 
