@@ -7,8 +7,9 @@ A step is one moe_ffn_forward over one batch: router, permute, grouped gate_up G
 the fused activation, grouped down GEMM and combine (and the shared expert when the
 workload has one). Inputs are seeded synthetic tensors already resident in HBM. W untimed
 steps, then K timed steps between two device synchronisations; rank 0 prints one JSON
-line. The dominant kernel (the grouped gate_up GEMM) is also timed on its own, launch by
-launch, with HIP events on the stream it runs on, for the roofline entry.
+line. For the roofline entry the dominant kernel (the grouped gate_up GEMM) is timed
+launch by launch with HIP events on the stream it runs on, inside complete layers run
+through the separate entry points.
 """
 import argparse
 import hashlib
@@ -127,17 +128,44 @@ def time_launches(call, reps: int, stream) -> float:
 
 
 def time_gate_up(cfg, d, reps: int):
-    """Average duration of one grouped gate_up GEMM launch, HIP events on its stream."""
+    """Average duration of the grouped gate_up GEMM launch, timed inside complete layers.
+
+    Each repetition runs the staged layer through the boundary's separate entry points
+    (route, permute, gate_up, down, combine: the kernels moe_ffn_forward launches) and
+    brackets only the gate_up launch with HIP events on its stream. Timing the kernel in a
+    loop of its own would measure it at the lower clock that back-to-back heavy GEMMs drive
+    the chip to, not at the one it runs at in the layer."""
     stream = torch.cuda.current_stream()
-    w, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize,
-                                                        cfg.rsf, cfg.G, cfg.TG),
-                               d.get("correction_bias"), d.get("expert_ids"))
-    off, srt, pos, _ = B.moe_permute(ids, cfg.E)
+    rcfg = B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG)
     act = torch.empty((cfg.T * cfg.K, cfg.F), dtype=cfg.torch_dtype, device="cuda")
-    call = lambda: B.moe_grouped_gemm_swiglu(d["hidden"], d["w_gate_up"], off, cfg.act,
-                                             d.get("b_gate_up"), a_rows=srt,
-                                             a_rows_div=cfg.K, out=act, stream=stream)
-    return time_launches(call, reps, stream), distinct_experts(ids)
+    y = torch.empty((cfg.T * cfg.K, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    out = torch.empty((cfg.T, cfg.H), dtype=cfg.torch_dtype, device="cuda")
+    ids = None
+
+    def layer(a=None, b=None):
+        nonlocal ids
+        w, ids, _, _ = B.moe_route(d["logits"], rcfg, d.get("correction_bias"),
+                                   d.get("expert_ids"), stream=stream)
+        off, srt, pos, _ = B.moe_permute(ids, cfg.E, stream=stream)
+        if a is not None:
+            a.record(stream)
+        B.moe_grouped_gemm_swiglu(d["hidden"], d["w_gate_up"], off, cfg.act,
+                                  d.get("b_gate_up"), a_rows=srt, a_rows_div=cfg.K, out=act,
+                                  stream=stream)
+        if b is not None:
+            b.record(stream)
+        B.moe_grouped_gemm(act, d["w_down"], off, d.get("b_down"), out=y, stream=stream)
+        B.moe_combine(y, w, pos, out=out, stream=stream)
+
+    for _ in range(3):
+        layer()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        layer(a, b)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ms)), distinct_experts(ids)
 
 
 def cpu_baseline(cfg, d, budget_s: float):
