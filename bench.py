@@ -29,6 +29,7 @@ from mixture_experts_ffn_moerouter_amd import inputs as I  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where the roofs meet
 METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 
 
@@ -89,6 +90,10 @@ def gate_up_algorithmic_bytes(cfg, n_experts: int) -> int:
     if cfg.bias_std is not None:
         b += n_experts * 2 * cfg.F * s
     return b + R * 4 + (cfg.E + 1) * 4
+
+
+def gate_up_flops(cfg) -> int:
+    return 2 * cfg.T * cfg.K * cfg.H * 2 * cfg.F
 
 
 def layer_algorithmic(cfg, n_experts: int):
@@ -168,6 +173,50 @@ def time_gate_up(cfg, d, reps: int):
     return float(np.mean(ms)), distinct_experts(ids)
 
 
+def router_line(cfg, args):
+    """Router-only workload: moe_route with the expert-parallel outputs, launch-bound.
+
+    value = tokens per second of one routing call; roofline against HBM over the bytes the
+    call must move (logits and bias in, ids, weights, router_probs and weight_scale out)."""
+    d = I.make_router_inputs(cfg, device="cuda")
+    rcfg = B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG,
+                       cfg.local_expert_start, cfg.local_expert_count or 0,
+                       cfg.router_probs_dtype or "f32")
+    stream = torch.cuda.current_stream()
+    call = lambda: B.moe_route(d["logits"], rcfg, d.get("correction_bias"),
+                               d.get("expert_ids"), with_router_probs=True, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = time_launches(call, args.kernel_reps, stream)
+    rp = 2 if cfg.router_probs_dtype in ("f16", "bf16") else 4
+    k_bytes = cfg.T * cfg.E * 4 + (cfg.E * 4 if cfg.correction_bias else 0) \
+        + cfg.T * cfg.K * 8 + cfg.T * (cfg.local_expert_count or 0) * rp + cfg.T * rp
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(cfg.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded SplitMix64/Box-Muller logits)",
+        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "top_k": cfg.K,
+                   "scoring": cfg.scoring, "local_expert_start": cfg.local_expert_start,
+                   "local_expert_count": cfg.local_expert_count,
+                   "router_probs_dtype": cfg.router_probs_dtype, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
+                     "traffic": None, "kernel": "route_kernel (launch-bound: tiny input)",
+                     "kernel_ms": round(k_ms, 5), "latency_us": round(k_ms * 1e3, 2),
+                     "algorithmic_bytes": k_bytes},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(cfg, d, budget_s: float):
     """The CPU oracle, as it stands, on the first n tokens of the same workload."""
     import oracle.moe_oracle as O
@@ -227,7 +276,9 @@ def main():
         return
     cfg = I.CONFIGS[args.workload]
     if cfg.H == 0:
-        sys.exit("router-only workload: not a bench line")
+        torch.cuda.set_device(0)
+        router_line(cfg, args)
+        return
     torch.cuda.set_device(0)
     log(f"[bench] {cfg.name}: generating inputs")
     d = I.make_inputs(cfg, device="cuda")
@@ -259,6 +310,7 @@ def main():
         log("[bench] timing the gate_up kernel")
         k_ms, _ = time_gate_up(cfg, d, args.kernel_reps)
         k_bytes = gate_up_algorithmic_bytes(cfg, n_exp)
+        k_flops = gate_up_flops(cfg)
         k_name = "gemm_bf16_kernel (grouped gate_up + SwiGLU)"
         k_traffic = recorded_traffic(cfg.name)
     else:
@@ -270,9 +322,17 @@ def main():
         k_ms = time_launches(lambda: run_layer(cfg, d, fcfg, ws, out, shared_out),
                              args.kernel_reps, stream)
         k_bytes = l_bytes
+        k_flops = l_flops
         k_name = "moe_ffn_forward, indexed backend (indexed_kernel gate_up + down dominate)"
         k_traffic = None
-    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    # the binding roof of the timed kernel: MFMA above the ridge, HBM below it
+    if k_flops / k_bytes > RIDGE:
+        roof = {"bound": "mfma", "achieved": round(k_flops / (k_ms * 1e-3) / 1e12, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     line = {
         "metric": METRIC,
         "value": round(tokens_per_s, 1),
@@ -290,11 +350,9 @@ def main():
                    "top_k": cfg.K, "scoring": cfg.scoring, "activation": cfg.act,
                    "num_expert_group": cfg.G, "topk_group": cfg.TG, "F_shared": cfg.F_s,
                    "backend": backend, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": k_name,
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": k_traffic,
-                     "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes},
+        "roofline": {**roof, "traffic": k_traffic, "kernel": k_name,
+                     "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes,
+                     "algorithmic_flops": k_flops},
         "layer": {"hbm_frac": round(l_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                   "mfma_frac": round(l_flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
                   "algorithmic_bytes": l_bytes, "flops": l_flops,

@@ -140,6 +140,7 @@ class MoEConfig:
     local_expert_count: Optional[int] = None
     router_probs_dtype: Optional[str] = None
     hash_routing: bool = False
+    logit_skew: float = 0.0                     # logits[:, e] += logit_skew * e / (E - 1)
     notes: str = field(default="", compare=False)
 
     @property
@@ -166,6 +167,12 @@ CONFIGS = {
     "dsv3_bf16": MoEConfig("dsv3_bf16", T=4096, H=7168, E=256, F=2048, K=8,
                            scoring="sigmoid", rsf=2.5, G=8, TG=4,
                            correction_bias=(-0.1, 0.1), F_s=2048),
+    # Compute-bound evidence point (not a graded workload): the Qwen3 shapes at four times
+    # the tokens, ~1024 routes per expert, arithmetic intensity above the ridge.
+    "qwen3_bf16_t16k": MoEConfig("qwen3_bf16_t16k", T=16384, H=2048, E=128, F=768, K=8),
+    # Skewed expert load (a per-expert logit offset): a few experts take most tokens.
+    "qwen3_skewed_bf16": MoEConfig("qwen3_skewed_bf16", T=4096, H=2048, E=128, F=768, K=8,
+                                   logit_skew=6.0),
     "decode_dsv3_bf16": MoEConfig("decode_dsv3_bf16", T=16, H=7168, E=256, F=2048, K=8,
                                   scoring="sigmoid", rsf=2.5, G=8, TG=4,
                                   correction_bias=(-0.1, 0.1)),
@@ -179,6 +186,9 @@ CONFIGS = {
 def make_router_inputs(cfg: MoEConfig, *, seed: int = 0, device="cpu") -> dict:
     d = {"logits": normal((cfg.T, cfg.E), cfg.logit_std, seed=seed,
                           stream=STREAMS["logits"], dtype=torch.float32, device=device)}
+    if cfg.logit_skew:
+        ramp = torch.arange(cfg.E, dtype=torch.float32, device=device) / max(cfg.E - 1, 1)
+        d["logits"] += cfg.logit_skew * ramp
     if cfg.correction_bias is not None:
         lo, hi = cfg.correction_bias
         d["correction_bias"] = uniform((cfg.E,), lo, hi, seed=seed,

@@ -33,6 +33,8 @@ SMALL = {
     "decode_many_routes_per_expert": I.MoEConfig("decode_many", T=40, H=384, E=24, F=512,
                                                  K=1, renormalize=False),
     "single_token": I.MoEConfig("single_token", T=1, H=128, E=4, F=64, K=2),
+    # a per-expert logit ramp: some experts take most tokens, many take none
+    "skewed_load": I.MoEConfig("skewed_load", T=600, H=320, E=48, F=192, K=6, logit_skew=6.0),
 }
 
 
@@ -126,9 +128,10 @@ def test_ffn_zero_tokens():
 
 
 # Full-size workloads: every output computed on the GPU, sampled tokens checked.
-FULL = ["tiny_fp32", "qwen3_bf16", "gptoss_bf16", "dsv3_bf16", "decode_dsv3_bf16"]
+FULL = ["tiny_fp32", "qwen3_bf16", "gptoss_bf16", "dsv3_bf16", "decode_dsv3_bf16",
+        "qwen3_skewed_bf16"]
 SAMPLES = {"tiny_fp32": 64, "qwen3_bf16": 12, "gptoss_bf16": 8, "dsv3_bf16": 4,
-           "decode_dsv3_bf16": 6}
+           "decode_dsv3_bf16": 6, "qwen3_skewed_bf16": 8}
 
 
 @pytest.mark.parametrize("name", FULL)
