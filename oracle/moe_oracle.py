@@ -36,7 +36,7 @@ __all__ = [
     "routing_weights", "ep_router_outputs", "RouteResult", "route", "swiglu",
     "ACTIVATIONS", "split_gate_up", "expert_mlp", "grouped_gemm", "grouped_gemm_act",
     "permute", "combine", "shared_expert_mlp", "moe_ffn_forward",
-    "indexed_backend_applies", "PARITY_STATUS",
+    "indexed_backend_applies", "decode_e4m3fn", "grouped_gemm_fp8_masked", "PARITY_STATUS",
 ]
 
 # --------------------------------------------------------------------------------------
@@ -452,6 +452,58 @@ def indexed_backend_applies(T: int, K: int, E: int, H: int, F: int, activation: 
             and H % 128 == 0 and F % 256 == 0)
 
 
+# --------------------------------------------------------------------------------------
+# Block-scaled FP8 grouped GEMM over a masked slab.
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """float8_e4m3fn codes (bytes) to float64 values.
+
+    [TO] MoEGroupedGemmFP8FwdOp types both operands float8_e4m3fn: the E4M3 encoding of
+    the OCP 8-bit floating point formats. Bit 7 is the sign, bits 6..3 the exponent with
+    bias 7, bits 2..0 the mantissa. Exponent field 0 holds the subnormals m/8 * 2^-6.
+    There are no infinities: only the all-ones exponent with all-ones mantissa is NaN,
+    so exponent 15 with mantissa 0..6 are ordinary values up to 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def grouped_gemm_fp8_masked(a_codes, a_scale, b_codes, b_scale, counts) -> np.ndarray:
+    """[TO] MoEGroupedGemmFP8FwdOp: one block-scaled FP8 GEMM per expert over a masked slab.
+
+    a [E, max_m, K] and b [E, N, K] are float8_e4m3fn codes; a_scale [E, max_m, K/128]
+    holds one float32 per row and 128 columns of a, b_scale [E, N/128, K/128] one per
+    128 x 128 block of b; K and N are multiples of 128. Expert g has m_g valid rows,
+    counts[g] read as max_m past max_m and as 0 below 0. For each 128-wide K block kb the
+    raw FP8 values are contracted, the block sum is multiplied by its two scales
+    a_scale[g, m, kb] * b_scale[g, n // 128, kb], and the products are added up:
+        out[g, m, n] = sum_kb (sum_{k in kb} a[g,m,k] b[g,n,k]) a_scale[g,m,kb] b_scale[g,n//128,kb]
+    stored in bfloat16. Rows at or past m_g are undefined on the page; they are NaN here.
+    Sums are float64 (the page's accuracy reference is the dequantized product).
+    """
+    A = decode_e4m3fn(a_codes)
+    B = decode_e4m3fn(b_codes)
+    sa = np.asarray(a_scale, dtype=np.float64)
+    sb = np.asarray(b_scale, dtype=np.float64)
+    E, max_m, K = A.shape
+    N = B.shape[1]
+    out = np.full((E, max_m, N), np.nan)
+    for g in range(E):
+        m = int(min(max(int(counts[g]), 0), max_m))
+        acc = np.zeros((m, N))
+        for kb in range(K // 128):
+            ks = slice(128 * kb, 128 * (kb + 1))
+            block = A[g, :m, ks] @ B[g, :, ks].T
+            acc += block * sa[g, :m, kb][:, None] * np.repeat(sb[g, :, kb], 128)[None, :]
+        out[g, :m] = round_to(acc, "bf16")
+    return out
+
+
 # What pins each function (the tests under tests/ named test_oracle_*.py). Functions
 # whose parity rests only on a reading of the pages say so.
 PARITY_STATUS = {
@@ -467,5 +519,8 @@ PARITY_STATUS = {
     "combine": "pinned: brute-force per-element sums",
     "shared_expert_mlp": "pinned: torch float64 dense MLP with rounding points",
     "moe_ffn_forward": "pinned: soft-mixture special case, per-token brute force",
+    "decode_e4m3fn": "pinned: torch float8_e4m3fn decode of all 256 codes, format constants",
+    "grouped_gemm_fp8_masked": "pinned: dequantize-then-multiply brute force, exact small "
+                               "integers, count clamping",
     "sqrt_softplus reading": "parity unpinned beyond the reading sqrt(softplus(z))",
 }

@@ -465,4 +465,82 @@ def pin_dispatch_rule():
     assert not O.indexed_backend_applies(16, 8, 256, 7168, 2048 + 128, "silu_and_mul", False)
 
 
+# ------------------------------------------------------------------- FP8 grouped GEMM
+def pin_e4m3fn_decode():
+    """All 256 codes against torch's float8_e4m3fn, plus the format's landmarks."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.decode_e4m3fn(codes)
+    want = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, want, equal_nan=True)
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0      # largest finite
+    assert got[0x08] == 2.0 ** -6 and got[0x01] == 2.0 ** -9  # min normal, min subnormal
+    assert got[0x38] == 1.0 and got[0x00] == 0.0 and np.signbit(got[0x80])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.isnan(got).sum() == 2
+
+
+def _fp8_case(seed, E, max_m, K, N):
+    r = _rng(seed)
+    a = r.integers(0, 256, (E, max_m, K), dtype=np.uint8)
+    b = r.integers(0, 256, (E, N, K), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38  # no NaN codes in operands
+    b[(b & 0x7F) == 0x7F] = 0x30
+    sa = r.uniform(0.25, 4.0, (E, max_m, K // 128))
+    sb = r.uniform(0.25, 4.0, (E, N // 128, K // 128))
+    return a, sa, b, sb
+
+
+def pin_fp8_gemm_dequantized_bruteforce():
+    """The page's accuracy reference: dequantize both operands under their scales
+    (every element times its own row / block scale), then one plain product per expert,
+    in torch float64; the oracle's block-wise order must agree to one bf16 step."""
+    E, max_m, K, N = 2, 5, 256, 256
+    a, sa, b, sb = _fp8_case(21, E, max_m, K, N)
+    counts = np.array([5, 3])
+    out = O.grouped_gemm_fp8_masked(a, sa, b, sb, counts)
+    A = torch.from_numpy(a).view(torch.float8_e4m3fn).to(torch.float64)
+    B = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64)
+    ka = torch.arange(K) // 128
+    for g in range(E):
+        deq_a = A[g] * torch.from_numpy(sa[g])[:, ka]
+        nb = torch.arange(N) // 128
+        deq_b = B[g] * torch.from_numpy(sb[g])[nb][:, ka]
+        want = (deq_a @ deq_b.T).numpy()
+        m = counts[g]
+        got = out[g, :m]
+        ulp = np.abs(O.round_to(want[:m], "bf16")) * 2.0 ** -7
+        assert np.all(np.abs(got - want[:m]) <= ulp + 1e-300)
+        assert np.isnan(out[g, m:]).all()
+
+
+def pin_fp8_gemm_exact_integers():
+    """Small integer codes and power-of-two scales: every product and partial sum is an
+    exact integer multiple of the scale, so the result equals an integer matmul."""
+    r = _rng(22)
+    E, max_m, K, N = 2, 4, 256, 128
+    vals = np.array([-3.0, -2.0, -1.0, 0.0, 1.0, 2.0, 3.0])
+    ia = r.integers(0, vals.size, (E, max_m, K))
+    ib = r.integers(0, vals.size, (E, N, K))
+    enc = torch.tensor(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    a, b = enc[ia], enc[ib]
+    sa = np.full((E, max_m, K // 128), 0.5)
+    sb = np.full((E, N // 128, K // 128), 4.0)
+    out = O.grouped_gemm_fp8_masked(a, sa, b, sb, np.array([max_m, max_m]))
+    for g in range(E):
+        want = (vals[ia[g]].astype(np.int64) @ vals[ib[g]].astype(np.int64).T) * 2.0
+        assert np.array_equal(out[g], O.round_to(want.astype(np.float64), "bf16"))
+    assert abs(O.round_to(np.array([257.0]), "bf16")[0] - 256.0) == 0  # the cast is real
+
+
+def pin_fp8_count_clamp():
+    """A count past max_m is read as max_m, a negative one as 0."""
+    E, max_m, K, N = 4, 3, 128, 128
+    a, sa, b, sb = _fp8_case(23, E, max_m, K, N)
+    out = O.grouped_gemm_fp8_masked(a, sa, b, sb, np.array([-2, 0, max_m + 5, 2]))
+    assert np.isnan(out[0]).all() and np.isnan(out[1]).all()
+    assert not np.isnan(out[2]).any()
+    assert not np.isnan(out[3, :2]).any() and np.isnan(out[3, 2:]).all()
+    full = O.grouped_gemm_fp8_masked(a, sa, b, sb, np.array([max_m] * E))
+    assert np.array_equal(out[2], full[2])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

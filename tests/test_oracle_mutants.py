@@ -123,7 +123,47 @@ _orig_select = O.select_experts
 _orig_permute = O.permute
 _orig_ep = O.ep_router_outputs
 
+_orig_fp8 = O.grouped_gemm_fp8_masked
+_orig_decode = O.decode_e4m3fn
+
+
+def _decode_fnuz(codes):
+    # the other FP8 E4M3 encoding (exponent bias 8)
+    return _orig_decode(codes) / 2.0
+
+
+def _fp8_block_scale_tiled(a_codes, a_scale, b_codes, b_scale, counts):
+    # b_scale expanded along n by tiling (n % blocks) instead of n // 128
+    A = O.decode_e4m3fn(a_codes)
+    B = O.decode_e4m3fn(b_codes)
+    E, max_m, K = A.shape
+    N = B.shape[1]
+    out = np.full((E, max_m, N), np.nan)
+    for g in range(E):
+        m = int(min(max(int(counts[g]), 0), max_m))
+        acc = np.zeros((m, N))
+        for kb in range(K // 128):
+            ks = slice(128 * kb, 128 * (kb + 1))
+            acc += (A[g, :m, ks] @ B[g, :, ks].T) * a_scale[g, :m, kb][:, None] * \
+                np.tile(b_scale[g, :, kb], 128)[None, :N]
+        out[g, :m] = O.round_to(acc, "bf16")
+    return out
+
+
+def _fp8_counts_unclamped(a_codes, a_scale, b_codes, b_scale, counts):
+    return _orig_fp8(a_codes, a_scale, b_codes, b_scale, np.abs(np.asarray(counts)))
+
+
+def _fp8_no_a_scale(a_codes, a_scale, b_codes, b_scale, counts):
+    return _orig_fp8(a_codes, np.ones_like(np.asarray(a_scale)), b_codes, b_scale, counts)
+
+
 MUTANTS = {
+    "fp8 decoded with bias 8": ("decode_e4m3fn", _decode_fnuz),
+    "fp8 b scale tiled along n": ("grouped_gemm_fp8_masked", _fp8_block_scale_tiled),
+    "fp8 negative count read as its magnitude": ("grouped_gemm_fp8_masked",
+                                                 _fp8_counts_unclamped),
+    "fp8 a scale dropped": ("grouped_gemm_fp8_masked", _fp8_no_a_scale),
     "gate clamped from below too": ("swiglu", _swiglu_two_sided_gate),
     "limit<=0 does not disable the clamp": ("swiglu", _swiglu_no_disable),
     "gate and up halves swapped": ("split_gate_up", _split_swapped),
