@@ -271,6 +271,31 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
                     float* topk_weights_out, int32_t* topk_ids_out, void* workspace,
                     size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------
+ * moe_grouped_gemm_fp8_masked - block-scaled FP8 GEMM per expert over a masked slab:
+ * out[g, :m_g] = a[g, :m_g] b[g]^T.
+ * [TO] MoEGroupedGemmFP8FwdOp (float8_e4m3fn operands, per-row x 128 and per-128x128
+ * float32 scales applied once per 128-wide K block, bfloat16 result).
+ *
+ * a        [E, max_m, K] float8_e4m3fn (OCP E4M3) bytes; expert g's rows are g*max_m ...
+ * a_scale  [E, max_m, K/128] float32: one scale per row and 128 columns of a.
+ * b        [E, N, K] float8_e4m3fn bytes (rows contiguous in K).
+ * b_scale  [E, N/128, K/128] float32: one scale per 128 x 128 block of b.
+ * counts   [E] int32 on the device: valid rows m_g of expert g, read as max_m when larger
+ *          and as 0 when negative; not checked (a check would synchronise).
+ * out      [E, max_m, N] bfloat16: for m < m_g, out[g, m, n] = sum over 128-wide K blocks
+ *          kb of (sum_{k in kb} a[g,m,k] b[g,n,k]) * a_scale[g,m,kb] * b_scale[g,n/128,kb],
+ *          accumulated in float32 and rounded once (ties to even). Rows at or past m_g are
+ *          left unwritten.
+ * Limits: K and N multiples of 128, E <= 1024, max_m*K and N*K below 2^31 bytes (32-bit
+ * offsets within one expert). max_m == 0 does nothing.
+ * Errors: INVALID_ARG (null pointer, non-positive size), UNSUPPORTED (K or N not a multiple
+ * of 128, limits), OVERLAP (out vs a, a_scale, b, b_scale, counts).
+ * ------------------------------------------------------------------------------- */
+int moe_grouped_gemm_fp8_masked(const void* a, const float* a_scale, const void* b,
+                                const float* b_scale, const int32_t* counts, int64_t E,
+                                int64_t max_m, int64_t K, int64_t N, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

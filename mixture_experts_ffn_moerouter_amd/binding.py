@@ -30,7 +30,8 @@ ACTIVATIONS = {"silu_and_mul": (0, 1.0, 0.0, 0.0), "swigluoai": (1, 1.702, 1.0, 
 SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute_workspace_size",
            "moe_permute",
            "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
-           "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward")
+           "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward",
+           "moe_grouped_gemm_fp8_masked")
 
 
 class MoeRouteCfg(ctypes.Structure):
@@ -98,6 +99,9 @@ def lib():
         L.moe_ffn_workspace_size.argtypes = [ctypes.POINTER(MoeFfnCfg)]
         L.moe_ffn_backend.restype = ctypes.c_int
         L.moe_ffn_backend.argtypes = [ctypes.POINTER(MoeFfnCfg), ctypes.c_int]
+        L.moe_grouped_gemm_fp8_masked.restype = ctypes.c_int
+        L.moe_grouped_gemm_fp8_masked.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                                                  _P, _P]
         L.moe_ffn_forward.restype = ctypes.c_int
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(MoeFfnCfg)] + [_P] * 15 + \
             [ctypes.c_size_t, _P]
@@ -241,6 +245,25 @@ def moe_combine(y, topk_weights, route_pos, scale: float = 1.0, out_dtype=None, 
     _check("moe_combine", lib().moe_combine(
         _ptr(y), TORCH_DTYPES[y.dtype], _ptr(topk_weights), _ptr(route_pos), T, K, H,
         float(scale), _ptr(out), TORCH_DTYPES[out_dtype], _stream(stream)))
+    return out
+
+
+def _fp8_bytes(t):
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def moe_grouped_gemm_fp8_masked(a, a_scale, b, b_scale, counts, out=None, stream=None):
+    """a [E, max_m, K] and b [E, N, K] as float8_e4m3fn or their uint8 bytes; a_scale
+    [E, max_m, K/128] and b_scale [E, N/128, K/128] float32; counts [E] int32. Returns
+    out [E, max_m, N] bfloat16 (rows at or past a count are left as they were)."""
+    a, b = _fp8_bytes(a), _fp8_bytes(b)
+    E, max_m, K = a.shape
+    N = b.shape[1]
+    out = torch.empty((E, max_m, N), dtype=torch.bfloat16, device=a.device) \
+        if out is None else out
+    _check("moe_grouped_gemm_fp8_masked", lib().moe_grouped_gemm_fp8_masked(
+        _ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale), _ptr(counts), E, max_m, K, N,
+        _ptr(out), _stream(stream)))
     return out
 
 

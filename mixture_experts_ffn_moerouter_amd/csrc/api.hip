@@ -283,6 +283,35 @@ int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, i
                              expert_offsets, dt, out_dt, out, stream);
 }
 
+int moe_grouped_gemm_fp8_masked(const void* a, const float* a_scale, const void* b,
+                                const float* b_scale, const int32_t* counts, int64_t E,
+                                int64_t max_m, int64_t K, int64_t N, void* out, void* stream) {
+  if (E < 1 || max_m < 0 || K < 1 || N < 1) return MOE_ERR_INVALID_ARG;
+  if (!b || !b_scale || !counts) return MOE_ERR_INVALID_ARG;
+  if (max_m > 0 && (!a || !a_scale || !out)) return MOE_ERR_INVALID_ARG;
+  if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
+  if (max_m * K >= ((int64_t)1 << 31) || N * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  const size_t e = (size_t)E, m = (size_t)max_m, k = (size_t)K, n = (size_t)N;
+  Range ins[] = {{a, e * m * k}, {a_scale, e * m * (k / 128) * 4}, {b, e * n * k},
+                 {b_scale, e * (n / 128) * (k / 128) * 4}, {counts, e * 4}};
+  Range outs[] = {{out, e * m * n * 2}};
+  if (any_overlap(outs, 1, ins, 5)) return MOE_ERR_OVERLAP;
+  if (max_m == 0) return MOE_OK;
+  Fp8GemmArgs g;
+  g.a = (const uint8_t*)a;
+  g.a_scale = a_scale;
+  g.b = (const uint8_t*)b;
+  g.b_scale = b_scale;
+  g.counts = counts;
+  g.E = (int)E;
+  g.max_m = (int)max_m;
+  g.K = (int)K;
+  g.N = (int)N;
+  g.out = (uint16_t*)out;
+  return status_of(launch_gemm_fp8_masked(g, (hipStream_t)stream));
+}
+
 int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
                 const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
                 void* out, int32_t out_dt, void* stream) {

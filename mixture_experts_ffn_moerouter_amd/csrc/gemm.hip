@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "tile_map.h"
 
 namespace moe {
 namespace {
@@ -60,58 +61,6 @@ __device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float b
     l = fminf(fmaxf(l, -limit), limit);
   }
   return g * (1.0f / (1.0f + __expf(-alpha * g))) * (l + beta);
-}
-
-// Tiles of an expert with `rows` rows, and the rows per tile (a multiple of 32).
-__device__ __forceinline__ int tiles_of(int rows, int bm) { return (rows + bm - 1) / bm; }
-__device__ __forceinline__ int rows_per_tile(int rows, int bm) {
-  const int n = tiles_of(rows, bm);
-  return n ? ((rows + n - 1) / n + 31) / 32 * 32 : 0;
-}
-
-// Builds s_pre[0..E] = exclusive prefix of per-expert tile counts and copies the offsets
-// into s_off. offsets == NULL means one expert that owns rows 0 .. M-1. All NT threads.
-template <int NT>
-__device__ void build_tile_map(const int32_t* offsets, int E, int M, int bm, int* s_off,
-                               int* s_pre, int* s_tmp) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int W = NT / 64;
-  for (int i = tid; i <= E; i += NT) s_off[i] = offsets ? offsets[i] : (i == 0 ? 0 : M);
-  __syncthreads();
-  int carry = 0;
-  for (int e0 = 0; e0 < E; e0 += NT) {
-    const int e = e0 + tid;
-    const int c = e < E ? tiles_of(s_off[e + 1] - s_off[e], bm) : 0;
-    int x = c;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
-    }
-    if (lane == 63) s_tmp[wave] = x;
-    __syncthreads();
-    int wbase = 0, chunk = 0;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      wbase += w < wave ? s_tmp[w] : 0;
-      chunk += s_tmp[w];
-    }
-    if (e < E) s_pre[e] = carry + wbase + x - c;
-    carry += chunk;
-    __syncthreads();
-  }
-  if (tid == 0) s_pre[E] = carry;
-  __syncthreads();
-}
-
-// Largest e with s_pre[e] <= tile (s_pre non-decreasing, s_pre[0] = 0).
-__device__ __forceinline__ int find_expert(const int* s_pre, int E, int tile) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (s_pre[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {

@@ -99,4 +99,16 @@ struct IndexedArgs {
 };
 hipError_t launch_indexed_mlp(const IndexedArgs& a, hipStream_t s);
 
+// Block-scaled FP8 grouped GEMM over a masked slab (bf16 out).
+struct Fp8GemmArgs {
+  const uint8_t* a;       // [E, max_m, K] e4m3fn
+  const float* a_scale;   // [E, max_m, K/128]
+  const uint8_t* b;       // [E, N, K] e4m3fn
+  const float* b_scale;   // [E, N/128, K/128]
+  const int32_t* counts;  // [E]
+  int E, max_m, K, N;
+  uint16_t* out;          // [E, max_m, N] bf16
+};
+hipError_t launch_gemm_fp8_masked(const Fp8GemmArgs& g, hipStream_t s);
+
 }  // namespace moe

@@ -32,6 +32,7 @@ _CHUNK = 1 << 24
 STREAMS = {
     "hidden": 0, "logits": 1, "w_gate_up": 2, "w_down": 3, "b_gate_up": 4, "b_down": 5,
     "correction_bias": 6, "shared_w_gate_up": 7, "shared_w_down": 8, "expert_ids": 9,
+    "fp8_a": 10, "fp8_b": 11, "fp8_counts": 12,
 }
 
 
@@ -71,13 +72,14 @@ def _uniform(key: int, counters: torch.Tensor) -> torch.Tensor:
     return _shr(uniform_words(key, counters), 11).to(torch.float64) * (2.0 ** -53)
 
 
-def _fill(out: torch.Tensor, key: int, kind: str, a: float, b: float) -> torch.Tensor:
+def _fill(out: torch.Tensor, key: int, kind: str, a: float, b: float,
+          start: int = 0) -> torch.Tensor:
     flat = out.view(-1)
     n = flat.numel()
     dev = out.device
     for lo in range(0, n, _CHUNK):
         hi = min(n, lo + _CHUNK)
-        i = torch.arange(lo, hi, dtype=torch.int64, device=dev)
+        i = torch.arange(start + lo, start + hi, dtype=torch.int64, device=dev)
         if kind == "normal":
             u1 = _uniform(key, 2 * i)
             u2 = _uniform(key, 2 * i + 1)
@@ -92,9 +94,11 @@ def _fill(out: torch.Tensor, key: int, kind: str, a: float, b: float) -> torch.T
 
 
 def normal(shape, std: float, *, seed: int, stream: int, dtype=torch.float32,
-           device="cpu", mean: float = 0.0) -> torch.Tensor:
+           device="cpu", mean: float = 0.0, start: int = 0) -> torch.Tensor:
+    """Elements start, start+1, ... of the stream (start lets a large tensor be made in
+    pieces that equal the corresponding slices of the whole)."""
     out = torch.empty(shape, dtype=dtype, device=device)
-    return _fill(out, stream_key(seed, stream), "normal", mean, std)
+    return _fill(out, stream_key(seed, stream), "normal", mean, std, start)
 
 
 def uniform(shape, lo: float, hi: float, *, seed: int, stream: int, dtype=torch.float32,
@@ -222,3 +226,72 @@ def make_inputs(cfg: MoEConfig, *, seed: int = 0, device="cpu") -> dict:
                                     stream=STREAMS["shared_w_down"], dtype=dt,
                                     device=device)
     return d
+
+
+# --------------------------------------------------------------------------------------
+# Block-scaled FP8 grouped GEMM over a masked slab (a [E, max_m, K], b [E, N, K]).
+
+@dataclass(frozen=True)
+class Fp8GemmConfig:
+    """One FP8 masked grouped GEMM workload. counts, when given, fixes the valid rows of
+    each expert; otherwise they are round(N(rows_mean, rows_std)) clamped to [0, max_m]."""
+    name: str
+    E: int
+    max_m: int
+    K: int
+    N: int
+    rows_mean: float = 0.0
+    rows_std: float = 0.0
+    counts: Optional[tuple] = None
+    a_std: float = 1.0
+    b_std: float = 0.02
+    notes: str = field(default="", compare=False)
+
+
+FP8_CONFIGS = {
+    # small parity case: empty, single-row, ragged, full and over-full experts
+    "fp8_small": Fp8GemmConfig("fp8_small", E=7, max_m=160, K=384, N=384,
+                               counts=(0, 1, 37, 128, 129, 160, 200)),
+    # the DeepSeek-V3 routed expert GEMMs in the masked layout: about 128 routes per
+    # expert (T 4096, top-8 of 256), slabs of 256 rows
+    "dsv3_fp8_gate_up": Fp8GemmConfig("dsv3_fp8_gate_up", E=256, max_m=256, K=7168, N=4096,
+                                      rows_mean=128.0, rows_std=11.1),
+    "dsv3_fp8_down": Fp8GemmConfig("dsv3_fp8_down", E=256, max_m=256, K=2048, N=7168,
+                                   rows_mean=128.0, rows_std=11.1),
+}
+
+
+def _quantize_e4m3fn_blocks(x: torch.Tensor, rows_per_block: int):
+    """x [R, K] float32 -> (codes [R, K] uint8, scales [R/rows_per_block, K/128] float32):
+    each rows_per_block x 128 block is divided by amax/448 (1 for an all-zero block) and
+    cast to float8_e4m3fn (round to nearest even)."""
+    R, K = x.shape
+    xb = x.view(R // rows_per_block, rows_per_block, K // 128, 128)
+    amax = xb.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (xb / scale[:, None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+    return q.view(R, K).view(torch.uint8), scale.to(torch.float32)
+
+
+def make_fp8_inputs(cfg: Fp8GemmConfig, *, seed: int = 0, device="cpu") -> dict:
+    """a, a_scale, b, b_scale (codes as uint8) and counts of one FP8 workload, generated
+    one expert at a time."""
+    E, M, K, N = cfg.E, cfg.max_m, cfg.K, cfg.N
+    a = torch.empty((E, M, K), dtype=torch.uint8, device=device)
+    b = torch.empty((E, N, K), dtype=torch.uint8, device=device)
+    sa = torch.empty((E, M, K // 128), dtype=torch.float32, device=device)
+    sb = torch.empty((E, N // 128, K // 128), dtype=torch.float32, device=device)
+    for g in range(E):
+        xa = normal((M, K), cfg.a_std, seed=seed, stream=STREAMS["fp8_a"], device=device,
+                    start=g * M * K)
+        a[g], sa[g] = _quantize_e4m3fn_blocks(xa, 1)
+        xb = normal((N, K), cfg.b_std, seed=seed, stream=STREAMS["fp8_b"], device=device,
+                    start=g * N * K)
+        b[g], sb[g] = _quantize_e4m3fn_blocks(xb, 128)
+    if cfg.counts is not None:
+        counts = torch.tensor(cfg.counts, dtype=torch.int32, device=device)
+    else:
+        c = normal((E,), cfg.rows_std, seed=seed, stream=STREAMS["fp8_counts"],
+                   dtype=torch.float64, device=device, mean=cfg.rows_mean)
+        counts = c.round().clamp(0, M).to(torch.int32)
+    return {"a": a, "a_scale": sa, "b": b, "b_scale": sb, "counts": counts}

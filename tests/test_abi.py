@@ -24,7 +24,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(B.SYMBOLS)
     L = B.lib()
     for n in names:
@@ -164,3 +164,22 @@ def test_ffn_argument_errors():
     assert ffn(f16, a) == B.MOE_ERR_UNSUPPORTED
     forced = B.ffn_cfg(I.CONFIGS["tiny_fp32"], "indexed")
     assert ffn(forced, a) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_fp8_masked_gemm_argument_errors():
+    L = B.lib()
+    A, SA, W, SW, C, OUT = (FAKE + i * (1 << 34) for i in range(6))
+    f = lambda E=2, m=4, K=256, N=128, a=A, sa=SA, w=W, sw=SW, c=C, out=OUT: \
+        L.moe_grouped_gemm_fp8_masked(a, sa, w, sw, c, E, m, K, N, out, None)
+    assert f(K=200) == B.MOE_ERR_UNSUPPORTED          # K not a multiple of 128
+    assert f(N=100) == B.MOE_ERR_UNSUPPORTED          # N not a multiple of 128
+    assert f(E=0) == B.MOE_ERR_INVALID_ARG
+    assert f(m=-1) == B.MOE_ERR_INVALID_ARG
+    assert f(w=None) == B.MOE_ERR_INVALID_ARG
+    assert f(c=None) == B.MOE_ERR_INVALID_ARG
+    assert f(a=None) == B.MOE_ERR_INVALID_ARG
+    assert f(E=2000) == B.MOE_ERR_UNSUPPORTED
+    assert f(m=1 << 16, K=1 << 15) == B.MOE_ERR_UNSUPPORTED   # slab past 2^31 bytes
+    assert f(out=A + 64) == B.MOE_ERR_OVERLAP         # out over a
+    assert f(out=C) == B.MOE_ERR_OVERLAP              # out over counts
+    assert f(m=0, a=None, sa=None, out=None) == B.MOE_OK  # nothing to do, nothing launched
