@@ -29,6 +29,7 @@ from mixture_experts_ffn_moerouter_amd import inputs as I  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, TFLOP/s
 RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where the roofs meet
 METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 
@@ -217,6 +218,75 @@ def router_line(cfg, args):
     print(json.dumps(line), flush=True)
 
 
+def fp8_line(cfg, args):
+    """Block-scaled FP8 grouped GEMM over a masked slab (one step = one call). tokens =
+    valid rows / 8 (the workload is the top-8 routed GEMM of T tokens)."""
+    d = I.make_fp8_inputs(cfg, device="cuda")
+    out = torch.empty((cfg.E, cfg.max_m, cfg.N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: B.moe_grouped_gemm_fp8_masked(d["a"], d["a_scale"], d["b"], d["b_scale"],
+                                                 d["counts"], out=out, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = time_launches(call, args.kernel_reps, stream)
+    counts = d["counts"].cpu().numpy().astype(np.int64)
+    rows = int(counts.sum())
+    tokens = rows / 8.0
+    nkb = cfg.K // 128
+    k_bytes = rows * cfg.K + cfg.E * cfg.N * cfg.K + rows * nkb * 4 \
+        + cfg.E * (cfg.N // 128) * nkb * 4 + cfg.E * 4 + rows * cfg.N * 2
+    k_flops = 2 * rows * cfg.N * cfg.K
+    if k_flops / k_bytes > FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(k_flops / (k_ms * 1e-3) / 1e12, 1),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(k_bytes / (k_ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    line = {
+        "metric": METRIC, "value": round(tokens / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8 e4m3fn (block-scaled), fp32 accumulate, bf16 out",
+        "data": "synthetic (seeded SplitMix64/Box-Muller values, block-quantized to e4m3fn)",
+        "config": {"workload": cfg.name, "E": cfg.E, "max_m": cfg.max_m, "K": cfg.K,
+                   "N": cfg.N, "valid_rows": rows, "parallelism": "single GPU"},
+        "roofline": {**roof, "traffic": None,
+                     "kernel": "gemm_fp8_masked_kernel (block-scaled FP8 grouped GEMM)",
+                     "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes,
+                     "algorithmic_flops": k_flops},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        import oracle.moe_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        done, total, g = 0, 0.0, 0
+        while total < args.cpu_budget / 2 and g < cfg.E:
+            sub = {k: v[g:g + 1].cpu().numpy() for k, v in d.items() if k != "counts"}
+            t1 = time.perf_counter()
+            O.grouped_gemm_fp8_masked(sub["a"], sub["a_scale"], sub["b"], sub["b_scale"],
+                                      counts[g:g + 1])
+            total += time.perf_counter() - t1
+            done += int(counts[g])
+            g += 1
+        line["cpu_baseline"] = {
+            "value": done / 8.0 / total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"experts 0..{g - 1} of {cfg.E} ({done} of {rows} valid rows), float64 "
+                      f"numpy oracle, {total:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(cfg, d, budget_s: float):
     """The CPU oracle, as it stands, on the first n tokens of the same workload."""
     import oracle.moe_oracle as O
@@ -260,7 +330,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_bf16", choices=sorted(I.CONFIGS))
+    ap.add_argument("--workload", default="qwen3_bf16",
+                    choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS))
     ap.add_argument("--backend", default="auto", choices=["auto", "staged", "indexed"])
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -273,6 +344,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.workload in I.FP8_CONFIGS:
+        torch.cuda.set_device(0)
+        fp8_line(I.FP8_CONFIGS[args.workload], args)
         return
     cfg = I.CONFIGS[args.workload]
     if cfg.H == 0:
