@@ -8,24 +8,36 @@
 //      to a float32 accumulator; the result is stored in bfloat16. Rows at or past m_g
 //      are not written.
 //
-// Tile: 128 token rows x 128 weight rows (one b_scale block), eight waves (2 x 4) of 64
-// token rows x 32 weight rows, one workgroup per CU. A K step is one 128-wide scale block: 128 bytes of every row (the same bytes per
-// step as the bf16 kernel's 64-element step), staged through double-buffered LDS (row
-// stride 144 bytes: conflict-free 16-byte fragment reads) from registers loaded two steps
-// ahead with buffer loads (pieces past the tile or the matrix get an offset past the
-// buffer: zeros, no branch). The step's scales travel with it: threads 0..127 load the
-// a_scale of the tile's rows and thread 128 the b_scale of its weight block, into the same
-// LDS stage. A wave's 64 x 32 is 4 x 2 blocks of 16 x 16; each block
-// takes one v_mfma_scale_f32_16x16x128_f8f6f4 per step (neutral e8m0 scales, e4m3 on both
-// operands), which contracts the whole 128-wide scale block into a fresh accumulator; that
-// is multiplied by a_scale[row] * b_scale and added to the float32 accumulator, the order
-// the page gives. A lane holds 32 contiguous bytes of its row (lane quarter q: bytes
-// 32q .. 32q+31) for both operands, so products pair the same way on both sides and the
-// sum is the plain one.
+// Tile: 128 token rows x 256 weight rows (two b_scale blocks), eight waves (2 x 4) of 64 x
+// 64, one workgroup per CU. A K step is one 128-wide scale block: 128 bytes of every row.
+//
+// Staging. Three LDS stages form a ring filled by direct-to-LDS buffer loads (no register
+// staging, no LDS write instructions): step k + 2 is requested while step k is multiplied,
+// so each transfer has two steps to land. One load instruction moves 1 KB, eight rows x
+// 128 bytes (whole cache lines); lane l lands in row l / 8, 16-byte slot l % 8, and fetches
+// the row's byte piece (l % 8) ^ (row % 8), so slots are XOR-swizzled by row. The scales
+// of the step travel the same way (4-byte transfers: a_scale of the tile's rows, the two
+// b_scale blocks). A wave's seven transfers of the next step are spread through its MFMA
+// stream rather than issued at once. The compiler's workgroup barrier would wait for every
+// transfer in flight, so the step boundary is an explicit "own transfers of this step
+// landed (vmcnt), own LDS reads done, barrier" sequence.
+//
+// Multiply. Fragments are read with lane (r, q) of a 16-row block taking pieces q and q + 4
+// of row r (both operands alike, so products pair as in the plain sum); with the XOR slots
+// this read pattern is free of LDS bank conflicts. Each 16 x 16 block takes one
+// v_mfma_scale_f32_16x16x128_f8f6f4 per step (neutral e8m0 scales, e4m3 on both
+// operands) into a fresh accumulator, weights as the first operand, so a lane's four
+// results share one token row and one combined scale a_scale[row] * b_scale; that
+// product is folded into the float32 accumulator two MFMAs later, keeping the matrix
+// core fed while the vector unit applies the scales. This is the order the page gives:
+// per-block partial sums from the FP8 values, scaled, then accumulated in float32.
 //
 // Tile map: expert g with m_g rows gets ceil(m_g / 128) row tiles of equal height (rounded
 // up to 32 rows), built on the device from the counts; logical tiles are ordered expert,
-// n-tile, row tile and dealt so that consecutive ones run on one XCD.
+// n-tile, row tile and dealt so that consecutive ones run on one XCD (the row tiles of an
+// expert share its weight lines in that XCD's L2).
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "tile_map.h"
 
@@ -33,40 +45,40 @@ namespace moe {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kNT = 512, kWM = 2, kWN = 4, kRB = 2, kCB = 1;
-constexpr int kBMX = 32 * kRB * kWM;             // 128 token rows per tile
-constexpr int kBNW = 32 * kCB * kWN;             // 128 weight rows per tile
-constexpr int kStepBytes = 128;                  // bytes of a row per K step
-constexpr int kLDK = kStepBytes + 16;            // LDS row stride (bytes)
-constexpr int kCPR = kStepBytes / 16;            // 16-byte pieces per row segment
-constexpr int kRSTEP = kNT / kCPR;               // rows covered by one pass of the threads
-constexpr int kNLD = kBMX * kCPR / kNT;          // A pieces per thread per step
-constexpr int kNLDB = kBNW * kCPR / kNT;         // B pieces per thread per step
-constexpr int kScaleOff = (kBMX + kBNW) * kLDK;  // scales after the two tiles in a stage
-constexpr int kStageBytes = (kScaleOff + (kBMX + 1) * 4 + 15) / 16 * 16;
+constexpr int kNT = 512;                 // 8 waves: 2 (token rows) x 4 (weight rows)
+constexpr int kBMX = 128;                // token rows per tile
+constexpr int kBNW = 256;                // weight rows per tile
+constexpr int kNS = 3;                   // LDS stages
+constexpr int kA = 0;                    // stage layout (bytes): token rows
+constexpr int kB = kA + kBMX * 128;      // weight rows
+constexpr int kSA = kB + kBNW * 128;     // a_scale of the tile's rows
+constexpr int kSB = kSA + kBMX * 4;      // the two b_scale blocks (one 256-byte transfer)
+constexpr int kSink = kSB + 256;         // landing area of the idle waves' scale transfer
+constexpr int kStage = kSink + 256;
+constexpr int kPieces = 7;               // transfers per wave and step: 2 A, 4 B, 1 scale
+constexpr int kDepth = 2;                // MFMAs between a block's MFMA and its scaling
 constexpr int kMaxE = 1024;
 constexpr int kXcd = 8;
-constexpr uint32_t kOOB = 0x80000000u;
-static_assert(2 * kStageBytes >= 2 * (kMaxE + 1) * (int)sizeof(int), "tile map alias");
+constexpr uint32_t kOOB = 0x80000000u;   // byte offset past every buffer range used here
+static_assert(kNS * kStage >= 2 * (kMaxE + 1) * (int)sizeof(int), "tile map alias");
+static_assert(kNS * kStage + 64 <= 160 * 1024, "LDS");
 
-__device__ __forceinline__ i32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
 }
-__device__ __forceinline__ float ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
-__device__ __forceinline__ i32x8 lds32(const uint8_t* p) {
-  const i32x4 lo = *(const i32x4*)p, hi = *(const i32x4*)(p + 16);
-  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 4, off, 0, 0, 0);
 }
 
 __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) {
   __shared__ int s_tmp[kNT / 64];
-  extern __shared__ __align__(16) uint8_t smem[];  // [2][stage], tile map aliased first
+  extern __shared__ __align__(16) uint8_t smem[];  // [kNS][kStage], tile map aliased first
   int* s_cnt = (int*)smem;
   int* s_pre = s_cnt + kMaxE + 1;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = g.E, K = g.K, N = g.N, nkb = g.K / 128;
   build_tile_map_masked<kNT>(g.counts, E, g.max_m, kBMX, s_cnt, s_pre, s_tmp);
 
@@ -85,7 +97,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
   const int m0 = mt * rpt, m1 = min(m0 + rpt, cnt);
   const int rows = m1 - m0;
   const int nb = (rows + 31) / 32;
-  __syncthreads();  // every thread has read the map; the buffers become stages
+  __syncthreads();  // every thread has read the map; the buffer becomes the stages
 
   // Buffer resources over expert e's slabs (32-bit offsets within one expert).
   const int64_t M = g.max_m;
@@ -99,136 +111,141 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
       (void*)(g.b_scale + (int64_t)e * (N / 128) * nkb), (short)0, (int)((N / 128) * nkb * 4),
       0x00020000);
 
-  // Thread tid moves 16-byte piece tid % 8 of rows tid / 8 + 64 i of both tiles.
-  const int kc = (tid % kCPR) * 16;
-  uint32_t aoff[kNLD], boff[kNLDB];
+  // Wave w moves 1 KB pieces 2w, 2w + 1 of the token tile (rows 16w .. 16w + 15) and
+  // 4w .. 4w + 3 of the weight tile (rows 32w .. 32w + 31). Rows past the tile or the
+  // matrix get an offset past the buffer; what lands for them is never stored.
+  const int prow = lane >> 3;
+  const uint32_t pbyte = 16u * (uint32_t)((lane & 7) ^ prow);
+  uint32_t aoff[2], boff[4];
 #pragma unroll
-  for (int i = 0; i < kNLD; ++i) {
-    const int r = tid / kCPR + kRSTEP * i;
-    aoff[i] = r < rows ? (uint32_t)(m0 + r) * (uint32_t)K + kc : kOOB;
+  for (int u = 0; u < 2; ++u) {
+    const int r = 8 * (2 * wave + u) + prow;
+    aoff[u] = r < rows ? (uint32_t)(m0 + r) * (uint32_t)K + pbyte : kOOB;
   }
 #pragma unroll
-  for (int i = 0; i < kNLDB; ++i) {
-    const int wr = nt * kBNW + tid / kCPR + kRSTEP * i;
-    boff[i] = wr < N ? (uint32_t)wr * (uint32_t)K + kc : kOOB;
+  for (int u = 0; u < 4; ++u) {
+    const int wr = nt * kBNW + 8 * (4 * wave + u) + prow;
+    boff[u] = wr < N ? (uint32_t)wr * (uint32_t)K + pbyte : kOOB;
   }
-  // the tile's rows of a_scale (threads 0..127) and its b_scale block (thread 128)
-  const uint32_t soa = tid < rows ? (uint32_t)(m0 + tid) * nkb * 4u : kOOB;
-  const uint32_t sob = tid == kBMX ? (uint32_t)nt * nkb * 4u : kOOB;
-
-  i32x4 xa0[kNLD], xa1[kNLD], xb0[kNLDB], xb1[kNLDB];
-  float xs0, xs1;
-  auto load = [&](int kb, i32x4* xa, i32x4* xb, float& xs) {
+  // Scales: waves 0 and 1 move the a_scale of rows 64 w + lane, wave 2 the two b_scale
+  // blocks of the tile; the other waves' transfer is empty (keeps the count uniform).
+  uint32_t soff = kOOB;
+  __amdgpu_buffer_rsrc_t rs = rsb;
+  int sdst = kSink;
+  if (wave < 2) {
+    const int r = 64 * wave + lane;
+    soff = r < rows ? (uint32_t)(m0 + r) * nkb * 4u : kOOB;
+    rs = rsa;
+    sdst = kSA + 256 * wave;
+  } else if (wave == 2) {
+    const int blk = nt * 2 + lane;
+    soff = (lane < 2 && blk < N / 128) ? (uint32_t)blk * nkb * 4u : kOOB;
+    sdst = kSB;
+  }
+  // transfer p of this wave's share of step kb (steps past the end move nothing)
+  auto piece = [&](int kb, int p) {
+    uint8_t* st = smem + (kb % kNS) * kStage;
     const bool in = kb < nkb;
-    const uint32_t k0 = (uint32_t)kb * kStepBytes;
-#pragma unroll
-    for (int i = 0; i < kNLD; ++i) xa[i] = ld16(ra, in ? aoff[i] + k0 : kOOB);
-#pragma unroll
-    for (int i = 0; i < kNLDB; ++i) xb[i] = ld16(rb, in ? boff[i] + k0 : kOOB);
-    const float sa = ld4(rsa, in ? soa + 4u * kb : kOOB);
-    const float sb = ld4(rsb, in ? sob + 4u * kb : kOOB);
-    xs = sa + sb;  // at most one of the two is in range for a thread
-  };
-  auto store = [&](int buf, const i32x4* xa, const i32x4* xb, float xs) {
-    uint8_t* la = smem + buf * kStageBytes;
-    uint8_t* lb = la + kBMX * kLDK;
-#pragma unroll
-    for (int i = 0; i < kNLD; ++i) *(i32x4*)(la + (tid / kCPR + kRSTEP * i) * kLDK + kc) = xa[i];
-#pragma unroll
-    for (int i = 0; i < kNLDB; ++i) *(i32x4*)(lb + (tid / kCPR + kRSTEP * i) * kLDK + kc) = xb[i];
-    if (tid <= kBMX) ((float*)(la + kScaleOff))[tid] = xs;
+    const uint32_t k0 = (uint32_t)kb * 128u;
+    if (p < 2) dma16(ra, st + kA + (2 * wave + p) * 1024, in ? aoff[p] + k0 : kOOB);
+    else if (p < 6) dma16(rb, st + kB + (4 * wave + p - 2) * 1024, in ? boff[p - 2] + k0 : kOOB);
+    else dma4(rs, st + sdst, in ? soff + 4u * (uint32_t)kb : kOOB);
   };
 
-  // Wave (wm, wn): its 32-row blocks wm and wm + 2 of the tile, as 16-row blocks
-  // rowblk(i) = (wm + 2 (i / 2)) 32 + 16 (i % 2), i < 4; weight rows wn*32 + 16 j, j < 2.
-  const int wm = wave % kWM, wn = wave / kWM;
-  const int lr = lane & 15, lq = (lane >> 4) * 32;  // operand row, byte quarter
-  auto rowblk = [&](int i) { return (wm + kWM * (i >> 1)) * 32 + 16 * (i & 1); };
-  const int nbw = nb > wm ? (nb - wm + kWM - 1) / kWM : 0;  // live 32-row blocks of this wave
+  // Wave (wm, wn): token 16-row blocks rowblk(i) = (wm + 2 (i / 2)) 32 + 16 (i % 2), weight
+  // rows wn 64 + 16 j. Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint32_t fo0 = 16u * (uint32_t)(lq ^ (lr & 7));
+  const uint32_t fo1 = 16u * (uint32_t)((lq ^ 4) ^ (lr & 7));
+  auto rowblk = [&](int i) { return (wm + 2 * (i >> 1)) * 32 + 16 * (i & 1); };
+  const int nbw = nb > wm ? (nb - wm + 1) / 2 : 0;  // live 32-row blocks of this wave
+  auto frag = [&](const uint8_t* rowp) {
+    const i32x4 lo = *(const i32x4*)(rowp + fo0), hi = *(const i32x4*)(rowp + fo1);
+    return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
 
-  constexpr int NJ = 2;
-  f32x4 acc[4][NJ];
+  f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
-  auto main_loop = [&](auto nbw_c) {
-    constexpr int NI = 2 * decltype(nbw_c)::value;  // live 16-row blocks
-    // One K step from LDS buffer buf: the weight fragments, then per row block the four
-    // MFMAs into fresh accumulators and their scaled accumulation. mid() (the store of
-    // the next step into the other buffer and the loads two steps ahead) follows the
-    // first row block.
-    auto compute = [&](int buf, auto&& mid) {
-      const uint8_t* la = smem + buf * kStageBytes;
-      const uint8_t* lb = la + kBMX * kLDK;
-      const float* sc = (const float*)(la + kScaleOff);
-      i32x8 fb[NJ];
+  auto main_loop = [&](auto ni_c) {
+    constexpr int NI = decltype(ni_c)::value;  // live 16-row blocks
+    constexpr int NB = NI * 4;                 // MFMAs per step
+    constexpr int EVERY = NB >= 2 * kPieces ? 2 : 1;
+    static_assert(EVERY * (kPieces - 1) < NB + kDepth, "every transfer is issued");
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[j] = lds32(lb + (wn * 32 + 16 * j + lr) * kLDK + lq);
-      const float sbv = sc[kBMX];
+    for (int p = 0; p < kPieces; ++p) piece(0, p);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int rb = rowblk(i);
-        const i32x8 fa = lds32(la + (rb + lr) * kLDK + lq);
-        f32x4 s4 = *(const f32x4*)(sc + rb + 4 * (lane >> 4));
+    for (int p = 0; p < kPieces; ++p) piece(1, p);
+    for (int kb = 0; kb < nkb; ++kb) {
+      // This wave's transfers of step kb have landed (those of kb + 1 may not have) and
+      // its reads of step kb - 1 are done; after the barrier every wave's are, so stage
+      // kb % 3 is complete and stage (kb + 2) % 3 is free.
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPieces) : "memory");
+      const uint8_t* st = smem + (kb % kNS) * kStage;
+      // every operand of the step, in the order the MFMAs consume them
+      i32x8 fa[NI], fb[4];
+      float sa[NI], s1[NI];
+      const float sbv = *(const float*)(st + kSB + 4 * (wn >> 1));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s4[q] *= sbv;
+      for (int i = 0; i < NI; ++i) sa[i] = *(const float*)(st + kSA + 4 * (rowblk(i) + lr));
+      __builtin_amdgcn_sched_barrier(0);
+      fa[0] = frag(st + kA + (rowblk(0) + lr) * 128);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const f32x4 blk = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-              fa, fb[j], f32x4{}, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[i][j][q] = fmaf(blk[q], s4[q], acc[i][j][q]);
-        }
-        if (i == 0) {
-          __builtin_amdgcn_sched_barrier(0);
-          mid();
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int j = 0; j < 4; ++j) {
+        fb[j] = frag(st + kB + (wn * 64 + 16 * j + lr) * 128);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    auto none = [] {};
-    // Step s uses LDS buffer s % 2 and register set s % 2; after storing step k+1 the
-    // loads of step k+3 go into the set just freed, so one step of loads stays in flight
-    // across every wait. Steps past the end load nothing (out-of-range offsets).
-    load(0, xa0, xb0, xs0);
-    load(1, xa1, xb1, xs1);
-    store(0, xa0, xb0, xs0);
-    load(2, xa0, xb0, xs0);
-    __syncthreads();
-    int k = 0;
-    for (; k + 1 < nkb; k += 2) {
-      compute(0, [&] {
-        store(1, xa1, xb1, xs1);
-        load(k + 3, xa1, xb1, xs1);
-      });
-      __syncthreads();
-      compute(1, [&] {
-        store(0, xa0, xb0, xs0);
-        load(k + 4, xa0, xb0, xs0);
-      });
-      __syncthreads();
-    }
-    if (k < nkb) compute(0, none);  // odd number of steps: the last one is in buffer 0
-  };
-  if (nbw >= 2) main_loop(std::integral_constant<int, 2>{});
-  else main_loop(std::integral_constant<int, 1>{});
-
-  // Epilogue: register q of lane l holds row 4*(l/16) + q and column l%16 of its 16 x 16
-  // block.
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = nt * kBNW + wn * 32 + 16 * j + lr;
+      for (int i = 1; i < NI; ++i) {
+        fa[i] = frag(st + kA + (rowblk(i) + lr) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) s1[i] = sa[i] * sbv;
+      // MFMA t, the scaling of block t - kDepth, and every EVERY-th slot one transfer of
+      // step kb + 2, in this order (pinned against the scheduler)
+      f32x4 blk[NB];
+#pragma unroll
+      for (int t = 0; t < NB + kDepth; ++t) {
+        if (t < NB)
+          blk[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              fb[t % 4], fa[t / 4], f32x4{}, 0, 0, 0, 127, 0, 127);
+        if (t >= kDepth) {
+          const int u = t - kDepth;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[u / 4][u % 4][q] = fmaf(blk[u][q], s1[u / 4], acc[u / 4][u % 4][q]);
+        }
+        if (t % EVERY == EVERY - 1 && t / EVERY < kPieces) piece(kb + 2, t / EVERY);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // no transfer into LDS may outlive the workgroup
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+  if (nbw >= 2) main_loop(std::integral_constant<int, 4>{});
+  else main_loop(std::integral_constant<int, 2>{});
+
+  // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
+  // wn 64 + 16 j + 4 q .. + 3: one 8-byte store each.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = nt * kBNW + wn * 64 + 16 * j + 4 * lq;
     if (n < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < 2 * nbw) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int m = m0 + rowblk(i) + 4 * (lane >> 4) + q;
-            if (m < m1) g.out[((int64_t)e * M + m) * N + n] = f32_to_bf16(acc[i][j][q]);
-          }
+        const int m = m0 + rowblk(i) + lr;
+        if (i < 2 * nbw && m < m1) {
+          const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) |
+                              ((uint32_t)f32_to_bf16(acc[i][j][3]) << 16);
+          *(uint2*)(g.out + ((int64_t)e * M + m) * N + n) = make_uint2(lo, hi);
         }
       }
     }
@@ -243,7 +260,7 @@ hipError_t launch_gemm_fp8_masked(const Fp8GemmArgs& g, hipStream_t s) {
   const int64_t max_tiles = (int64_t)g.E * ((g.max_m + kBMX - 1) / kBMX);
   int64_t grid = max_tiles * n_tiles_n;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  const size_t lds = 2 * (size_t)kStageBytes;
+  const size_t lds = (size_t)kNS * kStage;
   hipError_t err = hipFuncSetAttribute((const void*)gemm_fp8_masked_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
