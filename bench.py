@@ -12,6 +12,7 @@ launch by launch with HIP events on the stream it runs on, inside complete layer
 through the separate entry points.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -34,28 +35,39 @@ RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where th
 METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)"
 
 
-# HBM bytes of one grouped gate_up launch, read by the FETCH_SIZE and WRITE_SIZE counters
-# (rocprofv3 --pmc, one counter per run, over this script's own launches) and scaled by
-# what the same counters read for a plain copy of known size (--copy-calibration). The
-# figure belongs to the kernel source it was measured on: gemm_src is the SHA-256 of
-# csrc/gemm.hip at the time, and a different source reports null.
+# HBM bytes of one launch of a workload's dominant GEMM, read by the FETCH_SIZE and
+# WRITE_SIZE counters (rocprofv3 --pmc, one counter per run, over this script's own
+# launches; FP8 workloads with --host-inputs) and scaled by what the same counters read for
+# a plain copy of known size (--copy-calibration). A figure belongs to the kernel source it
+# was measured on: gemm_src is the SHA-256 of that kernel's file and csrc/tile_map.h at the
+# time, and a different source reports null.
 TRAFFIC = {
-    # FETCH_SIZE 529162.9 KiB x 1.99995 + WRITE_SIZE 49153.0 KiB x 1.0 per launch; the 1 GiB
-    # copy read 524301.3 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE.
-    "qwen3_bf16": {"gemm_src": "7349f9934277d1db207905bedca1cca4d1fc235a9567ff401c2f8b8a27913ccf",
-                   "bytes": 1134030807},
+    # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
+    # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE).
+    # gate_up: 528790.5 + 49152.9 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1133268249,
+                   "gemm_src": "19afab5a2e42ccf7c0d5a33d7016ddd43f3a8e506bba2c1fe7caafc8aa735301"},
+    # 4512238.0 + 263745.7 KiB
+    "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9510906364,
+                         "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
+    # 1909139.3 + 463106.7 KiB
+    "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4384040110,
+                      "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
 }
 
 
-def gemm_source_digest() -> str:
-    path = os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", "gemm.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def gemm_source_digest(kernel: str = "gemm.hip") -> str:
+    """SHA-256 over a GEMM kernel's source and the tile-map header it includes."""
+    h = hashlib.sha256()
+    for name in (kernel, "tile_map.h"):
+        with open(os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload: str):
     rec = TRAFFIC.get(workload)
-    if rec is None or rec["gemm_src"] != gemm_source_digest():
+    if rec is None or rec["gemm_src"] != gemm_source_digest(rec.get("kernel", "gemm.hip")):
         return None
     return rec["bytes"]
 
@@ -221,7 +233,16 @@ def router_line(cfg, args):
 def fp8_line(cfg, args):
     """Block-scaled FP8 grouped GEMM over a masked slab (one step = one call). tokens =
     valid rows / 8 (the workload is the top-8 routed GEMM of T tokens)."""
-    d = I.make_fp8_inputs(cfg, device="cuda")
+    if args.host_inputs:
+        # Counter runs: expert 0 is generated on the host and copied to every expert, so
+        # the profiled process launches no generator kernels (the byte traffic of the GEMM
+        # does not depend on the values).
+        one = I.make_fp8_inputs(dataclasses.replace(cfg, E=1, counts=(0,)), device="cpu")
+        d = {k: one[k].expand(cfg.E, *one[k].shape[1:]).contiguous().to("cuda")
+             for k in ("a", "a_scale", "b", "b_scale")}
+        d["counts"] = I.fp8_counts(cfg, device="cpu").to("cuda")
+    else:
+        d = I.make_fp8_inputs(cfg, device="cuda")
     out = torch.empty((cfg.E, cfg.max_m, cfg.N), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     call = lambda: B.moe_grouped_gemm_fp8_masked(d["a"], d["a_scale"], d["b"], d["b_scale"],
@@ -257,7 +278,7 @@ def fp8_line(cfg, args):
         "data": "synthetic (seeded SplitMix64/Box-Muller values, block-quantized to e4m3fn)",
         "config": {"workload": cfg.name, "E": cfg.E, "max_m": cfg.max_m, "K": cfg.K,
                    "N": cfg.N, "valid_rows": rows, "parallelism": "single GPU"},
-        "roofline": {**roof, "traffic": None,
+        "roofline": {**roof, "traffic": recorded_traffic(cfg.name),
                      "kernel": "gemm_fp8_masked_kernel (block-scaled FP8 grouped GEMM)",
                      "kernel_ms": round(k_ms, 4), "algorithmic_bytes": k_bytes,
                      "algorithmic_flops": k_flops},
@@ -337,6 +358,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--host-inputs", action="store_true",
+                    help="FP8 workloads: replicate one host-generated expert (counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the path is built and measured on a single "

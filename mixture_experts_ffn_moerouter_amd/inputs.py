@@ -288,10 +288,15 @@ def make_fp8_inputs(cfg: Fp8GemmConfig, *, seed: int = 0, device="cpu") -> dict:
         xb = normal((N, K), cfg.b_std, seed=seed, stream=STREAMS["fp8_b"], device=device,
                     start=g * N * K)
         b[g], sb[g] = _quantize_e4m3fn_blocks(xb, 128)
+    return {"a": a, "a_scale": sa, "b": b, "b_scale": sb,
+            "counts": fp8_counts(cfg, seed=seed, device=device)}
+
+
+def fp8_counts(cfg: Fp8GemmConfig, *, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Valid rows per expert of an FP8 workload: cfg.counts, or round(N(rows_mean,
+    rows_std)) clamped to [0, max_m]."""
     if cfg.counts is not None:
-        counts = torch.tensor(cfg.counts, dtype=torch.int32, device=device)
-    else:
-        c = normal((E,), cfg.rows_std, seed=seed, stream=STREAMS["fp8_counts"],
-                   dtype=torch.float64, device=device, mean=cfg.rows_mean)
-        counts = c.round().clamp(0, M).to(torch.int32)
-    return {"a": a, "a_scale": sa, "b": b, "b_scale": sb, "counts": counts}
+        return torch.tensor(cfg.counts, dtype=torch.int32, device=device)
+    c = normal((cfg.E,), cfg.rows_std, seed=seed, stream=STREAMS["fp8_counts"],
+               dtype=torch.float64, device=device, mean=cfg.rows_mean)
+    return c.round().clamp(0, cfg.max_m).to(torch.int32)
