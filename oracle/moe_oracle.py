@@ -33,8 +33,9 @@ import numpy as np
 
 __all__ = [
     "FORMATS", "round_to", "sigmoid", "scores", "ranked", "select_experts",
-    "routing_weights", "ep_router_outputs", "RouteResult", "route", "swiglu",
-    "ACTIVATIONS", "split_gate_up", "expert_mlp", "grouped_gemm", "grouped_gemm_act",
+    "routing_weights", "ep_router_outputs", "RouteResult", "route", "swiglu", "gelu",
+    "gated", "swiglu_op", "ACTIVATIONS", "split_gate_up", "expert_mlp", "grouped_gemm",
+    "grouped_gemm_act",
     "permute", "combine", "shared_expert_mlp", "moe_ffn_forward",
     "indexed_backend_applies", "decode_e4m3fn", "grouped_gemm_fp8_masked", "PARITY_STATUS",
 ]
@@ -265,13 +266,48 @@ def swiglu(g, l, alpha: float = 1.0, beta: float = 0.0, limit: float = 0.0) -> n
     return g * sigmoid(alpha * g) * (l + beta)
 
 
-# name -> (row layout of gate_up, alpha, beta, limit).  [TO] MoEGroupedGemmFwdOp:
-# silu_and_mul reads gate rows then up rows and keeps silu(gate) * up; swigluoai reads
-# interleaved rows (2j gate, 2j+1 up) with fixed constants 1.702, 1, 7.
+def gelu(x) -> np.ndarray:
+    """x * Phi(x), Phi the standard normal distribution function, = x (1 + erf(x/sqrt 2))/2.
+
+    [TO] MoEGroupedGemmFwdOp names gelu_and_mul = act(gate) * up without fixing the GELU
+    form; the reading taken is the exact one (Hendrycks and Gimpel's definition), not the
+    tanh approximation.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
+
+
+# name -> (row layout of gate_up, alpha, beta, limit, kind).  [TO] MoEGroupedGemmFwdOp:
+# silu_and_mul and gelu_and_mul read gate rows then up rows and keep act(gate) * up;
+# swigluoai reads interleaved rows (2j gate, 2j+1 up) with fixed constants 1.702, 1, 7.
 ACTIVATIONS = {
-    "silu_and_mul": ("stacked", 1.0, 0.0, 0.0),
-    "swigluoai": ("interleaved", 1.702, 1.0, 7.0),
+    "silu_and_mul": ("stacked", 1.0, 0.0, 0.0, "swiglu"),
+    "swigluoai": ("interleaved", 1.702, 1.0, 7.0, "swiglu"),
+    "gelu_and_mul": ("stacked", 0.0, 0.0, 0.0, "gelu"),
 }
+
+
+def gated(g, l, params) -> np.ndarray:
+    """The gated activation of a (layout, alpha, beta, limit, kind) tuple on gate g and up l:
+    swiglu(g, l, alpha, beta, limit), or gelu(g) * l."""
+    _, alpha, beta, limit, kind = params
+    if kind == "gelu":
+        return gelu(g) * np.asarray(l, dtype=np.float64)
+    return swiglu(g, l, alpha, beta, limit)
+
+
+def swiglu_op(gate, up=None, alpha: float = 1.0, beta: float = 0.0, limit: float = 0.0,
+              fusion: str = "stacked", out_dtype: str = "f32") -> np.ndarray:
+    """[MR] SwiGLU operator: swiglu of gate and up, float arithmetic, stored in out_dtype.
+
+    With up given, gate and up are [.., F]. Without it gate is [.., 2F] holding both halves
+    of one projection: gate first, then up ([MR], fusion "stacked" = [SPEC] swiglu_fusion 2)
+    or interleaved per element pair ([SPEC] swiglu_fusion 1).
+    """
+    if up is None:
+        gate, up = split_gate_up(gate, fusion)
+    return round_to(swiglu(gate, up, alpha, beta, limit), out_dtype)
 
 
 def split_gate_up(h, layout: str):
@@ -292,7 +328,8 @@ def split_gate_up(h, layout: str):
 def _act_params(act):
     if isinstance(act, str):
         return ACTIVATIONS[act]
-    return tuple(act)  # (layout, alpha, beta, limit)
+    act = tuple(act)  # (layout, alpha, beta, limit[, kind])
+    return act if len(act) == 5 else act + ("swiglu",)
 
 
 def expert_mlp(x, w_gate_up, w_down, b_gate_up=None, b_down=None,
@@ -305,13 +342,14 @@ def expert_mlp(x, w_gate_up, w_down, b_gate_up=None, b_down=None,
     ([CPU] expert-major, output-major; [SPEC] column-major [H, 2F] storage is the same
     bytes). y is returned unrounded.
     """
-    layout, alpha, beta, limit = _act_params(act)
+    params = _act_params(act)
+    layout = params[0]
     x = np.asarray(x, dtype=np.float64)
     h = x @ np.asarray(w_gate_up, dtype=np.float64).T
     if b_gate_up is not None:
         h = h + np.asarray(b_gate_up, dtype=np.float64)[None, :]
     g, l = split_gate_up(h, layout)
-    a = round_to(swiglu(g, l, alpha, beta, limit), act_dtype)
+    a = round_to(gated(g, l, params), act_dtype)
     y = a @ np.asarray(w_down, dtype=np.float64).T
     if b_down is not None:
         y = y + np.asarray(b_down, dtype=np.float64)[None, :]
@@ -347,10 +385,10 @@ def grouped_gemm_act(a, b, expert_offsets, act="silu_and_mul", bias=None,
     order, the optional bias is [E, 2F] in the same order and joins before the
     activation; the output has F columns in out_dtype.
     """
-    layout, alpha, beta, limit = _act_params(act)
+    params = _act_params(act)
     h = grouped_gemm(a, b, expert_offsets, bias, "f64")
-    g, l = split_gate_up(h, layout)
-    return round_to(swiglu(g, l, alpha, beta, limit), out_dtype)
+    g, l = split_gate_up(h, params[0])
+    return round_to(gated(g, l, params), out_dtype)
 
 
 def permute(topk_ids, num_experts: int):
@@ -522,5 +560,12 @@ PARITY_STATUS = {
     "decode_e4m3fn": "pinned: torch float8_e4m3fn decode of all 256 codes, format constants",
     "grouped_gemm_fp8_masked": "pinned: dequantize-then-multiply brute force, exact small "
                                "integers, count clamping",
+    "gelu": "pinned: tabulated normal distribution function (15 decimals), torch's exact "
+            "GELU, GELU(x) - GELU(-x) = x",
+    "gated": "pinned: gelu_and_mul brute force against torch's GELU; swiglu as above",
+    "swiglu_op": "pinned: separate / stacked / interleaved forms agree, decimal closed "
+                 "forms, bf16 store against torch's cast",
     "sqrt_softplus reading": "parity unpinned beyond the reading sqrt(softplus(z))",
+    "gelu_and_mul reading": "the exact GELU is a reading (the pages name the activation "
+                            "only); pinned as that reading",
 }

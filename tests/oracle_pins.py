@@ -277,7 +277,7 @@ def _dswiglu(g, l, alpha, beta, limit):
 def pin_swiglu_closed_forms():
     oai = GOLDEN["swigluoai"]
     assert O.ACTIVATIONS["swigluoai"] == ("interleaved", oai["alpha"], oai["beta"],
-                                          oai["limit"])
+                                          oai["limit"], "swiglu")
     assert O.ACTIVATIONS["silu_and_mul"][0] == GOLDEN["silu_and_mul"]["layout"]
     cases = [((1.0, 1.0), (1.0, 0.0, 0.0), 0.7310585786300049),
              ((-2.0, 3.0), (1.0, 0.0, 0.0), -0.7152175321327052),
@@ -428,7 +428,7 @@ def pin_ffn_soft_mixture():
         want = np.zeros((T, H))
         for t in range(T):
             for e in range(E):
-                layout, al, be, li = O.ACTIVATIONS[act]
+                layout, al, be, li, _ = O.ACTIVATIONS[act]
                 h = wgu[e] @ x[t] + bgu[e]
                 g, u = (h[:F], h[F:]) if layout == "stacked" else (h[0::2], h[1::2])
                 if li > 0:
@@ -541,6 +541,71 @@ def pin_fp8_count_clamp():
     assert not np.isnan(out[3, :2]).any() and np.isnan(out[3, 2:]).all()
     full = O.grouped_gemm_fp8_masked(a, sa, b, sb, np.array([max_m] * E))
     assert np.array_equal(out[2], full[2])
+
+
+# ------------------------------------------------------- gelu_and_mul, SwiGLU op
+PHI = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                  "normal_cdf_table.json")))["phi"]
+
+
+def pin_gelu_table():
+    """GELU(x) = x Phi(x) against the tabulated normal distribution function (15 decimals):
+    separates the exact form from the tanh approximation (off by 1.5e-4 at x = 1)."""
+    for xs, phi in PHI.items():
+        x = float(xs)
+        for v, want in ((x, x * phi), (-x, -x * (1.0 - phi))):
+            got = float(O.gelu(np.array([v]))[0])
+            assert abs(got - want) <= 2e-15 * max(1.0, abs(want)), (v, got, want)
+    assert float(O.gelu(np.array([0.0]))[0]) == 0.0
+
+
+def pin_gelu_torch_and_symmetry():
+    """Against torch's exact GELU in float64, and GELU(x) - GELU(-x) = x."""
+    x = _rng(21).standard_normal(4000) * 4
+    got = O.gelu(x)
+    want = torch.nn.functional.gelu(torch.from_numpy(x), approximate="none").numpy()
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-15)
+    assert np.allclose(got - O.gelu(-x), x, rtol=0, atol=1e-12)
+
+
+def pin_gelu_and_mul_gemm():
+    """gelu_and_mul over a stacked gate_up: act(x Wg^T + bg) * (x Wu^T + bu) per expert,
+    with torch's exact GELU as the activation (brute-force product per expert)."""
+    r = _rng(22)
+    E, F, K = 3, 5, 7
+    off = np.array([0, 4, 4, 9])
+    a = _f32(r.standard_normal((9, K)))
+    b = _f32(r.standard_normal((E, 2 * F, K)))
+    bias = _f32(r.standard_normal((E, 2 * F)) * 0.1)
+    got = O.grouped_gemm_act(a, b, off, "gelu_and_mul", bias, "f64")
+    want = np.zeros((9, F))
+    for e in range(E):
+        for m in range(off[e], off[e + 1]):
+            h = torch.from_numpy(b[e] @ a[m] + bias[e])
+            want[m] = (torch.nn.functional.gelu(h[:F], approximate="none") * h[F:]).numpy()
+    assert np.allclose(got, want, rtol=1e-13, atol=1e-14)
+    assert O.ACTIVATIONS["gelu_and_mul"][0] == "stacked"
+
+
+def pin_swiglu_op_forms():
+    """[MR] SwiGLU op: separate gate/up, gate-then-up halves of one [.., 2F] input, and the
+    interleaved [SPEC] fusion 1 arrangement give the same values; the result is the
+    activation's closed form stored in the requested dtype."""
+    r = _rng(23)
+    g = _f32(r.standard_normal((6, 10)) * 4)
+    u = _f32(r.standard_normal((6, 10)) * 4)
+    for al, be, li in ((1.0, 0.0, 0.0), (1.702, 1.0, 7.0), (0.5, -0.25, 2.0)):
+        sep = O.swiglu_op(g, u, al, be, li, out_dtype="f64")
+        want = np.array([[float(_dswiglu(gi, ui, al, be, li)) for gi, ui in zip(gr, ur)]
+                         for gr, ur in zip(g, u)])
+        assert np.allclose(sep, want, rtol=1e-13, atol=1e-14)
+        st = O.swiglu_op(np.concatenate([g, u], axis=1), None, al, be, li, out_dtype="f64")
+        il = np.empty((6, 20))
+        il[:, 0::2], il[:, 1::2] = g, u
+        it = O.swiglu_op(il, None, al, be, li, fusion="interleaved", out_dtype="f64")
+        assert np.array_equal(st, sep) and np.array_equal(it, sep)
+        bf = O.swiglu_op(g, u, al, be, li, out_dtype="bf16")
+        assert np.array_equal(bf, torch.from_numpy(sep).to(torch.bfloat16).double().numpy())
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -2,6 +2,8 @@
 
 A pin suite that still passes with a mistake planted would not be pinning that part.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -158,7 +160,30 @@ def _fp8_no_a_scale(a_codes, a_scale, b_codes, b_scale, counts):
     return _orig_fp8(a_codes, np.ones_like(np.asarray(a_scale)), b_codes, b_scale, counts)
 
 
+_orig_gated = O.gated
+_orig_swiglu_op = O.swiglu_op
+
+
+def _gelu_tanh(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+def _gated_act_on_up(g, l, params):
+    if params[4] == "gelu":
+        return np.asarray(g, dtype=np.float64) * O.gelu(l)
+    return _orig_gated(g, l, params)
+
+
+def _swiglu_op_ignores_fusion(gate, up=None, alpha=1.0, beta=0.0, limit=0.0,
+                              fusion="stacked", out_dtype="f32"):
+    return _orig_swiglu_op(gate, up, alpha, beta, limit, "stacked", out_dtype)
+
+
 MUTANTS = {
+    "gelu by its tanh approximation": ("gelu", _gelu_tanh),
+    "gelu_and_mul activates the up half": ("gated", _gated_act_on_up),
+    "swiglu op reads interleaved input as stacked": ("swiglu_op", _swiglu_op_ignores_fusion),
     "fp8 decoded with bias 8": ("decode_e4m3fn", _decode_fnuz),
     "fp8 b scale tiled along n": ("grouped_gemm_fp8_masked", _fp8_block_scale_tiled),
     "fp8 negative count read as its magnitude": ("grouped_gemm_fp8_masked",
