@@ -26,8 +26,11 @@
  *     MoEPostPermuteFwdOp, MoEGroupedGemmFwdOp: overlap is rejected before writing).
  *   - Sizes of zero (T == 0, M == 0) return MOE_OK and launch nothing (moe_permute
  *     still writes its E+1 zero offsets); pointers to zero-sized buffers may be NULL.
- *   - dtypes: operands are MOE_F32 or MOE_BF16 (the same dtype for activations and
- *     weights); router logits and routing weights are float32.
+ *   - dtypes: operands are MOE_F32, MOE_BF16 or MOE_F16 (the same dtype for activations
+ *     and weights); router logits are float32, bfloat16 or float16 ([TO] FusedTopKFwdOp)
+ *     and are read exactly into float32; routing weights are float32.
+ *   - ABI version 2 (moe_abi_version): moe_route_cfg.logits_dtype and moe_act_cfg.kind
+ *     were added at the ends of those structs, and logits became `const void*`.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -65,7 +68,7 @@ typedef enum { MOE_GU_STACKED = 0, MOE_GU_INTERLEAVED = 1 } moe_gu_layout;
 typedef enum { MOE_BACKEND_AUTO = 0, MOE_BACKEND_STAGED = 1, MOE_BACKEND_INDEXED = 2 }
     moe_backend;
 
-/* Router options ([MR] MoERouter attributes; [TO] FusedTopKFwdOp __init__).
+/* Router options ([MR] MoERouter attributes; [TO] FusedTopKFwdOp __init__ and forward).
  *   top_k                 experts per token, 1 <= top_k <= min(E, 32)
  *   scoring               moe_scoring
  *   renormalize           nonzero: divide the chosen scores by their sum
@@ -76,7 +79,9 @@ typedef enum { MOE_BACKEND_AUTO = 0, MOE_BACKEND_STAGED = 1, MOE_BACKEND_INDEXED
  *                         groups must hold at least top_k experts
  *   local_expert_start/count  the expert-parallel slice [start, start+count) that
  *                         router_probs describes (0 <= start, start+count <= E)
- *   router_probs_dtype    moe_dtype of router_probs and weight_scale             */
+ *   router_probs_dtype    moe_dtype of router_probs and weight_scale
+ *   logits_dtype          moe_dtype of the logits (each value is converted exactly to
+ *                         float32 before scoring)                                   */
 typedef struct {
   int32_t top_k;
   int32_t scoring;
@@ -87,18 +92,27 @@ typedef struct {
   int32_t local_expert_start;
   int32_t local_expert_count;
   int32_t router_probs_dtype;
+  int32_t logits_dtype;
 } moe_route_cfg;
+
+/* Kind of gated activation: the SwiGLU family, or gelu_and_mul. */
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_GELU_AND_MUL = 1 } moe_act_kind;
 
 /* Gated activation of the gate_up GEMM ([MR] SwiGLU; [SPEC] SwiGLU Activation
  * Function; [TO] MoEGroupedGemmFwdOp):
- *   out_j = G * sigmoid(alpha * G) * (L + beta),  G = min(gate_j, limit),
- *   L = clamp(up_j, -limit, limit); limit <= 0 turns both clamps off.
- * silu_and_mul = {STACKED, 1, 0, 0}; swigluoai = {INTERLEAVED, 1.702, 1, 7}. */
+ *   kind MOE_ACT_SWIGLU: out_j = G * sigmoid(alpha * G) * (L + beta),
+ *     G = min(gate_j, limit), L = clamp(up_j, -limit, limit); limit <= 0 turns both
+ *     clamps off. silu_and_mul = {STACKED, 1, 0, 0, SWIGLU};
+ *     swigluoai = {INTERLEAVED, 1.702, 1, 7, SWIGLU}.
+ *   kind MOE_ACT_GELU_AND_MUL: out_j = gelu(gate_j) * up_j with the exact GELU
+ *     x * Phi(x) (the pages name the activation only; the exact form is the reading
+ *     taken); STACKED layout only; alpha, beta and limit are ignored. */
 typedef struct {
   int32_t layout; /* moe_gu_layout */
   float alpha;
   float beta;
   float limit;
+  int32_t kind;   /* moe_act_kind */
 } moe_act_cfg;
 
 /* Whole-layer configuration for moe_ffn_forward. F_shared = 0: no shared expert.
@@ -114,14 +128,15 @@ typedef struct {
 /* Text of a status code. Host only; never fails. */
 const char* moe_status_str(int status);
 
-/* Library ABI version (this header: 1). Host only. */
+/* Library ABI version (this header: 2). Host only. */
 int moe_abi_version(void);
 
 /* ---------------------------------------------------------------------------------
  * moe_route - router: scores, selection, weights, expert-parallel outputs.
  * [MR] MoERouter; [TO] FusedTopKFwdOp and FusedMoEFwdOp (grouped routing).
  *
- * logits          [T, E] float32 router logits.
+ * logits          [T, E] router logits in cfg->logits_dtype (float32, bfloat16 or
+ *                 float16; [TO] FusedTopKFwdOp).
  * correction_bias [E] float32 or NULL. Added to the scores for the selection only
  *                 (noaux_tc); the weights use the unbiased scores.
  * expert_ids      [T, top_k] int32 or NULL. When given, it replaces the selection
@@ -144,7 +159,7 @@ int moe_abi_version(void);
  * Errors: INVALID_ARG for null logits/topk outputs, E < 1, E > 512, bad cfg fields;
  * OVERLAP if an output overlaps logits/bias/expert_ids or another output.
  * ------------------------------------------------------------------------------- */
-int moe_route(const float* logits, int64_t T, int64_t E, const float* correction_bias,
+int moe_route(const void* logits, int64_t T, int64_t E, const float* correction_bias,
               const int32_t* expert_ids, const moe_route_cfg* cfg, float* topk_weights,
               int32_t* topk_ids, void* router_probs, void* weight_scale, void* stream);
 
@@ -187,9 +202,9 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
  *                 expert_offsets[e+1]-1 (non-decreasing, expert_offsets[E] <= M).
  * out             [M, F] dt: act(a W_e^T + b_e) rounded to dt (ties to even). Rows not
  *                 covered by any expert are left unwritten.
- * Accumulation is float32. Limits: H % 8 == 0 for bf16 (16-byte rows), E <= 1024; for
- * bf16, M*H*2 and 2F*H*2 below 2^31 bytes (32-bit offsets; a gathered source must also
- * stay below 2^31 bytes).
+ * Accumulation is float32. Limits: H % 8 == 0 for bf16/f16 (16-byte rows), E <= 1024;
+ * for bf16/f16, M*H*2 and 2F*H*2 below 2^31 bytes (32-bit offsets; a gathered source
+ * must also stay below 2^31 bytes). INVALID_ARG for gelu_and_mul with INTERLEAVED rows.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP (out vs a, weights, bias, offsets, a_rows).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows_div,
@@ -207,7 +222,8 @@ int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows
  * b               [E, N, K] dt.   bias  [E, N] dt or NULL.
  * out             [M, N] in out_dt (dt or MOE_F32). Rows outside every expert are left
  *                 unwritten.
- * Limits: K % 8 == 0 for bf16, E <= 1024, M*K*2 and N*K*2 below 2^31 bytes for bf16.
+ * Limits: K % 8 == 0 for bf16/f16, E <= 1024, M*K*2 and N*K*2 below 2^31 bytes for
+ * bf16/f16.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP.
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, int64_t M,
@@ -230,6 +246,26 @@ int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
                 void* out, int32_t out_dt, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_swiglu - standalone SwiGLU operator.
+ * [MR] SwiGLU (float arithmetic whatever the storage type; optional up: without it gate
+ * holds both halves of one [.., 2F] projection, gate first, then up); [SPEC] Fusion
+ * Behavior (the fused projection may be interleaved instead).
+ *
+ * gate    [rows, F] in dt when up is given; else [rows, 2F] in dt, halves arranged per
+ *         fusion: MOE_GU_STACKED = [gate | up], MOE_GU_INTERLEAVED = element 2j gate j,
+ *         2j+1 up j.
+ * up      [rows, F] in dt, or NULL.
+ * out     [rows, F] in dt: G * sigmoid(alpha G) * (L + beta), G = min(gate, limit),
+ *         L = clamp(up, -limit, limit) (limit <= 0: no clamps), rounded to dt once.
+ * dt      MOE_F32, MOE_BF16 or MOE_F16 (inputs and output).
+ * Errors: INVALID_ARG (null pointer with rows > 0, F < 1, bad fusion), UNSUPPORTED
+ * (dtype, F >= 2^30), OVERLAP (out vs gate or up).
+ * ------------------------------------------------------------------------------- */
+int moe_swiglu(const void* gate, const void* up, int64_t rows, int64_t F, int32_t dt,
+               int32_t fusion, float alpha, float beta, float limit, void* out,
+               void* stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_ffn_workspace_size - bytes of device workspace moe_ffn_forward needs for cfg
  * (for either backend). Host only; returns 0 for an invalid cfg.
  * moe_ffn_backend - the backend moe_ffn_forward runs for cfg (MOE_BACKEND_STAGED or
@@ -246,7 +282,8 @@ int moe_ffn_backend(const moe_ffn_cfg* cfg, int has_bias);
  * [TO] FusedMoEFwdOp, FusedMoESharedExpertFwdOp, FusedMoEExpertsFwdOp,
  * IndexedExpertMLPFwdOp, SharedExpertMLPFwdOp; [MR] MoERouter.
  *
- * hidden [T, H] dt; logits [T, E] float32; correction_bias [E] float32 or NULL;
+ * hidden [T, H] dt; logits [T, E] in cfg->route.logits_dtype; correction_bias [E]
+ * float32 or NULL;
  * expert_ids [T, top_k] int32 or NULL (hash routing); w_gate_up [E, 2F, H] dt;
  * w_down [E, H, F] dt; b_gate_up [E, 2F] dt or NULL; b_down [E, H] dt or NULL;
  * shared_w_gate_up [2F_shared, H] dt (gate rows then up rows) and shared_w_down
@@ -263,7 +300,7 @@ int moe_ffn_backend(const moe_ffn_cfg* cfg, int has_bias);
  * The router_probs outputs of cfg->route are not produced here (use moe_route).
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP, WORKSPACE.
  * ------------------------------------------------------------------------------- */
-int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* logits,
+int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logits,
                     const float* correction_bias, const int32_t* expert_ids,
                     const void* w_gate_up, const void* w_down, const void* b_gate_up,
                     const void* b_down, const void* shared_w_gate_up,

@@ -23,15 +23,18 @@ TORCH_OF = {0: torch.float32, 1: torch.bfloat16, 2: torch.float16}
 SCORING = {"softmax": 0, "sigmoid": 1, "sqrt_softplus": 2}
 LAYOUTS = {"stacked": 0, "interleaved": 1}
 BACKENDS = {"auto": 0, "staged": 1, "indexed": 2}
-# name -> (layout, alpha, beta, limit); the constants swigluoai fixes.
-ACTIVATIONS = {"silu_and_mul": (0, 1.0, 0.0, 0.0), "swigluoai": (1, 1.702, 1.0, 7.0)}
+ABI_VERSION = 2
+# name -> (layout, alpha, beta, limit, kind); the constants swigluoai fixes; kind 1 is
+# gelu_and_mul (stacked rows, no constants).
+ACTIVATIONS = {"silu_and_mul": (0, 1.0, 0.0, 0.0, 0), "swigluoai": (1, 1.702, 1.0, 7.0, 0),
+               "gelu_and_mul": (0, 0.0, 0.0, 0.0, 1)}
 
 # Every symbol include/moe.h declares.
 SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute_workspace_size",
            "moe_permute",
            "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
            "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward",
-           "moe_grouped_gemm_fp8_masked")
+           "moe_grouped_gemm_fp8_masked", "moe_swiglu")
 
 
 class MoeRouteCfg(ctypes.Structure):
@@ -39,12 +42,12 @@ class MoeRouteCfg(ctypes.Structure):
                 ("renormalize", ctypes.c_int32), ("routed_scaling_factor", ctypes.c_float),
                 ("num_expert_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
                 ("local_expert_start", ctypes.c_int32), ("local_expert_count", ctypes.c_int32),
-                ("router_probs_dtype", ctypes.c_int32)]
+                ("router_probs_dtype", ctypes.c_int32), ("logits_dtype", ctypes.c_int32)]
 
 
 class MoeActCfg(ctypes.Structure):
     _fields_ = [("layout", ctypes.c_int32), ("alpha", ctypes.c_float),
-                ("beta", ctypes.c_float), ("limit", ctypes.c_float)]
+                ("beta", ctypes.c_float), ("limit", ctypes.c_float), ("kind", ctypes.c_int32)]
 
 
 class MoeFfnCfg(ctypes.Structure):
@@ -78,6 +81,9 @@ def lib():
         L.moe_status_str.argtypes = [ctypes.c_int]
         L.moe_abi_version.restype = ctypes.c_int
         L.moe_abi_version.argtypes = []
+        if L.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, this "
+                               f"binding needs {ABI_VERSION}; rebuild the library")
         L.moe_route.restype = ctypes.c_int
         L.moe_route.argtypes = [_P, _I64, _I64, _P, _P, ctypes.POINTER(MoeRouteCfg), _P, _P,
                                 _P, _P, _P]
@@ -102,6 +108,9 @@ def lib():
         L.moe_grouped_gemm_fp8_masked.restype = ctypes.c_int
         L.moe_grouped_gemm_fp8_masked.argtypes = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                                   _P, _P]
+        L.moe_swiglu.restype = ctypes.c_int
+        L.moe_swiglu.argtypes = [_P, _P, _I64, _I64, _I32, _I32, ctypes.c_float,
+                                 ctypes.c_float, ctypes.c_float, _P, _P]
         L.moe_ffn_forward.restype = ctypes.c_int
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(MoeFfnCfg)] + [_P] * 15 + \
             [ctypes.c_size_t, _P]
@@ -140,11 +149,14 @@ def route_cfg(top_k: int, scoring: str = "softmax", renormalize: bool = False,
 
 
 def act_cfg(act) -> MoeActCfg:
-    """'silu_and_mul', 'swigluoai', or a (layout, alpha, beta, limit) tuple."""
+    """'silu_and_mul', 'swigluoai', 'gelu_and_mul', or a (layout, alpha, beta, limit[,
+    kind]) tuple."""
     if isinstance(act, str):
         return MoeActCfg(*ACTIVATIONS[act])
-    layout, alpha, beta, limit = act
-    return MoeActCfg(LAYOUTS[layout] if isinstance(layout, str) else layout, alpha, beta, limit)
+    layout, alpha, beta, limit = act[:4]
+    kind = act[4] if len(act) > 4 else 0
+    return MoeActCfg(LAYOUTS[layout] if isinstance(layout, str) else layout, alpha, beta, limit,
+                     kind)
 
 
 def ffn_cfg(cfg, backend: str = "auto") -> MoeFfnCfg:
@@ -161,6 +173,8 @@ def moe_route(logits, cfg: MoeRouteCfg, correction_bias=None, expert_ids=None,
     T, E = logits.shape
     K = cfg.top_k
     dev = logits.device
+    cfg = MoeRouteCfg.from_buffer_copy(cfg)
+    cfg.logits_dtype = TORCH_DTYPES[logits.dtype]
     topk_weights = torch.empty((T, K), dtype=torch.float32, device=dev) \
         if topk_weights is None else topk_weights
     topk_ids = torch.empty((T, K), dtype=torch.int32, device=dev) if topk_ids is None \
@@ -267,6 +281,20 @@ def moe_grouped_gemm_fp8_masked(a, a_scale, b, b_scale, counts, out=None, stream
     return out
 
 
+def moe_swiglu(gate, up=None, alpha: float = 1.0, beta: float = 0.0, limit: float = 0.0,
+               fusion: str = "stacked", out=None, stream=None):
+    """[MR] SwiGLU: gate and up [.., F], or gate [.., 2F] holding both halves (fusion
+    'stacked' = gate then up, 'interleaved'). Returns out [.., F] in gate's dtype."""
+    F = gate.shape[-1] if up is not None else gate.shape[-1] // 2
+    rows = gate.numel() // max(1, gate.shape[-1])
+    out = torch.empty((*gate.shape[:-1], F), dtype=gate.dtype, device=gate.device) \
+        if out is None else out
+    _check("moe_swiglu", lib().moe_swiglu(
+        _ptr(gate), _ptr(up), rows, F, TORCH_DTYPES[gate.dtype], LAYOUTS[fusion],
+        float(alpha), float(beta), float(limit), _ptr(out), _stream(stream)))
+    return out
+
+
 def moe_ffn_workspace_size(cfg: MoeFfnCfg) -> int:
     return lib().moe_ffn_workspace_size(ctypes.byref(cfg))
 
@@ -282,6 +310,8 @@ def moe_ffn_forward(cfg: MoeFfnCfg, hidden, logits, w_gate_up, w_down, correctio
     """Returns (out, shared_out or None)."""
     T, H = hidden.shape
     dev = hidden.device
+    cfg = MoeFfnCfg.from_buffer_copy(cfg)
+    cfg.route.logits_dtype = TORCH_DTYPES[logits.dtype]
     out = torch.empty((T, H), dtype=hidden.dtype, device=dev) if out is None else out
     if cfg.F_shared > 0 and shared_out is None:
         shared_out = torch.empty((T, H), dtype=hidden.dtype, device=dev)

@@ -14,7 +14,7 @@ constexpr int kMaxGemmE = 1024;   // tile map and permute counters live in LDS
 constexpr int kMaxTopK = 32;
 
 size_t dt_size(int dt) { return dt == MOE_F32 ? 4 : 2; }
-bool operand_dt_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool operand_dt_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_F16; }
 bool any_dt_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_F16; }
 
 // Byte ranges [p, p+n) overlap? Empty ranges and null pointers never overlap.
@@ -46,6 +46,7 @@ int check_route_cfg(const moe_route_cfg* c, int64_t E, bool need_slice) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->top_k < 1 || c->top_k > E || c->top_k > kMaxTopK) return MOE_ERR_INVALID_ARG;
   if (c->scoring < 0 || c->scoring > 2) return MOE_ERR_INVALID_ARG;
+  if (!any_dt_ok(c->logits_dtype)) return MOE_ERR_INVALID_ARG;
   if (!(c->routed_scaling_factor > 0.f)) return MOE_ERR_INVALID_ARG;
   const int G = c->num_expert_group, TG = c->topk_group;
   if (G < 1 || G > 64 || E % G != 0) return MOE_ERR_INVALID_ARG;
@@ -60,12 +61,16 @@ int check_route_cfg(const moe_route_cfg* c, int64_t E, bool need_slice) {
   return MOE_OK;
 }
 
+// gelu_and_mul is defined over stacked rows only ([TO] MoEGroupedGemmFwdOp).
 bool act_ok(const moe_act_cfg* a) {
-  return a && (a->layout == MOE_GU_STACKED || a->layout == MOE_GU_INTERLEAVED);
+  if (!a || (a->layout != MOE_GU_STACKED && a->layout != MOE_GU_INTERLEAVED)) return false;
+  if (a->kind == MOE_ACT_GELU_AND_MUL) return a->layout == MOE_GU_STACKED;
+  return a->kind == MOE_ACT_SWIGLU;
 }
 
 bool is_silu_and_mul(const moe_act_cfg& a) {
-  return a.layout == MOE_GU_STACKED && a.alpha == 1.0f && a.beta == 0.0f && !(a.limit > 0.f);
+  return a.kind == MOE_ACT_SWIGLU && a.layout == MOE_GU_STACKED && a.alpha == 1.0f &&
+         a.beta == 0.0f && !(a.limit > 0.f);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -106,11 +111,11 @@ int check_ffn_cfg(const moe_ffn_cfg* c) {
   if (st) return st;
   if (!act_ok(&c->act)) return MOE_ERR_INVALID_ARG;
   if (c->E > kMaxRouteE) return MOE_ERR_UNSUPPORTED;
-  if (c->dtype == MOE_BF16 && (c->H % 8 || c->F % 8 || c->F_shared % 8))
+  if (c->dtype != MOE_F32 && (c->H % 8 || c->F % 8 || c->F_shared % 8))
     return MOE_ERR_UNSUPPORTED;
   // 32-bit byte offsets inside the GEMM tiles: hidden, act and one expert's weights
   const int64_t R = c->T * c->route.top_k, lim = (int64_t)1 << 31;
-  if (c->dtype == MOE_BF16 && (c->T * c->H * 2 >= lim || R * c->F * 2 >= lim ||
+  if (c->dtype != MOE_F32 && (c->T * c->H * 2 >= lim || R * c->F * 2 >= lim ||
                                2 * c->F * c->H * 2 >= lim || c->T * c->F_shared * 2 >= lim ||
                                2 * c->F_shared * c->H * 2 >= lim))
     return MOE_ERR_UNSUPPORTED;
@@ -118,7 +123,7 @@ int check_ffn_cfg(const moe_ffn_cfg* c) {
 }
 
 int backend_for(const moe_ffn_cfg& c, bool has_bias) {
-  const bool indexed_shape = c.dtype == MOE_BF16 && is_silu_and_mul(c.act) && !has_bias &&
+  const bool indexed_shape = c.dtype != MOE_F32 && is_silu_and_mul(c.act) && !has_bias &&
                              c.H % 128 == 0 && c.F % 256 == 0;
   if (c.backend == MOE_BACKEND_STAGED) return MOE_BACKEND_STAGED;
   if (c.backend == MOE_BACKEND_INDEXED) return indexed_shape ? MOE_BACKEND_INDEXED : -1;
@@ -142,9 +147,9 @@ const char* moe_status_str(int status) {
   }
 }
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
-int moe_route(const float* logits, int64_t T, int64_t E, const float* correction_bias,
+int moe_route(const void* logits, int64_t T, int64_t E, const float* correction_bias,
               const int32_t* expert_ids, const moe_route_cfg* cfg, float* topk_weights,
               int32_t* topk_ids, void* router_probs, void* weight_scale, void* stream) {
   if (!cfg || T < 0 || E < 1) return MOE_ERR_INVALID_ARG;
@@ -156,7 +161,8 @@ int moe_route(const float* logits, int64_t T, int64_t E, const float* correction
   if (T >= ((int64_t)1 << 31) / (E > cfg->top_k ? E : cfg->top_k)) return MOE_ERR_UNSUPPORTED;
   const size_t K = cfg->top_k;
   const size_t rps = router_probs ? dt_size(cfg->router_probs_dtype) : 0;
-  Range ins[] = {{logits, (size_t)T * E * 4}, {correction_bias, correction_bias ? (size_t)E * 4 : 0},
+  Range ins[] = {{logits, (size_t)T * E * dt_size(cfg->logits_dtype)},
+                 {correction_bias, correction_bias ? (size_t)E * 4 : 0},
                  {expert_ids, expert_ids ? (size_t)T * K * 4 : 0}};
   Range outs[] = {{topk_weights, (size_t)T * K * 4}, {topk_ids, (size_t)T * K * 4},
                   {router_probs, (size_t)T * (router_probs ? cfg->local_expert_count : 0) * rps},
@@ -165,6 +171,7 @@ int moe_route(const float* logits, int64_t T, int64_t E, const float* correction
   if (T == 0) return MOE_OK;
   RouteArgs a;
   a.logits = logits;
+  a.logits_dt = cfg->logits_dtype;
   a.bias = correction_bias;
   a.expert_ids = expert_ids;
   a.T = (int)T;
@@ -229,9 +236,9 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
   if (M >= ((int64_t)1 << 31) || Nw >= ((int64_t)1 << 30) || Kd >= ((int64_t)1 << 30))
     return MOE_ERR_UNSUPPORTED;
-  if (dt == MOE_BF16 && Kd % 8) return MOE_ERR_UNSUPPORTED;
-  // bf16 tiles address A and one expert's weights with 32-bit byte offsets
-  if (dt == MOE_BF16 && (M * Kd * 2 >= ((int64_t)1 << 31) || Nw * Kd * 2 >= ((int64_t)1 << 31)))
+  if (dt != MOE_F32 && Kd % 8) return MOE_ERR_UNSUPPORTED;
+  // 16-bit tiles address A and one expert's weights with 32-bit byte offsets
+  if (dt != MOE_F32 && (M * Kd * 2 >= ((int64_t)1 << 31) || Nw * Kd * 2 >= ((int64_t)1 << 31)))
     return MOE_ERR_UNSUPPORTED;
   if (dt == MOE_F32 && Kd > 12288) return MOE_ERR_UNSUPPORTED;  // A row staged in LDS
   const int64_t Nout = act_on ? Nw / 2 : Nw;
@@ -254,6 +261,7 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   g.E = (int)E;
   g.Nw = (int)Nw;
   g.act = act_on;
+  g.act_kind = act_on ? act->kind : 0;
   g.layout = act_on ? act->layout : 0;
   g.alpha = act_on ? act->alpha : 1.f;
   g.beta = act_on ? act->beta : 0.f;
@@ -312,6 +320,33 @@ int moe_grouped_gemm_fp8_masked(const void* a, const float* a_scale, const void*
   return status_of(launch_gemm_fp8_masked(g, (hipStream_t)stream));
 }
 
+int moe_swiglu(const void* gate, const void* up, int64_t rows, int64_t F, int32_t dt,
+               int32_t fusion, float alpha, float beta, float limit, void* out,
+               void* stream) {
+  if (rows < 0 || F < 1) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!gate || !out)) return MOE_ERR_INVALID_ARG;
+  if (!up && fusion != MOE_GU_STACKED && fusion != MOE_GU_INTERLEAVED) return MOE_ERR_INVALID_ARG;
+  if (!any_dt_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (F >= ((int64_t)1 << 30) || rows * F >= ((int64_t)1 << 40)) return MOE_ERR_UNSUPPORTED;
+  const size_t s = dt_size(dt), n = (size_t)rows * (size_t)F * s;
+  Range ins[] = {{gate, up ? n : 2 * n}, {up, up ? n : 0}};
+  Range outs[] = {{out, n}};
+  if (any_overlap(outs, 1, ins, 2)) return MOE_ERR_OVERLAP;
+  if (rows == 0) return MOE_OK;
+  SwigluArgs a;
+  a.gate = gate;
+  a.up = up;
+  a.rows = rows;
+  a.F = (int)F;
+  a.fusion = fusion;
+  a.dt = dt;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.limit = limit;
+  a.out = out;
+  return status_of(launch_swiglu(a, (hipStream_t)stream));
+}
+
 int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
                 const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
                 void* out, int32_t out_dt, void* stream) {
@@ -338,7 +373,7 @@ int moe_ffn_backend(const moe_ffn_cfg* cfg, int has_bias) {
   return backend_for(*cfg, has_bias != 0);
 }
 
-int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* logits,
+int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logits,
                     const float* correction_bias, const int32_t* expert_ids,
                     const void* w_gate_up, const void* w_down, const void* b_gate_up,
                     const void* b_down, const void* shared_w_gate_up,
@@ -362,7 +397,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
   const size_t s = dt_size(c.dtype), T = (size_t)c.T, H = (size_t)c.H, E = (size_t)c.E,
                F = (size_t)c.F, K = (size_t)c.route.top_k, Fs = (size_t)c.F_shared;
   Range ins[] = {{hidden, T * H * s},
-                 {logits, T * E * 4},
+                 {logits, T * E * dt_size(c.route.logits_dtype)},
                  {correction_bias, correction_bias ? E * 4 : 0},
                  {expert_ids, expert_ids ? T * K * 4 : 0},
                  {w_gate_up, E * 2 * F * H * s},
@@ -394,6 +429,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
   // 1. router
   RouteArgs ra;
   ra.logits = logits;
+  ra.logits_dt = c.route.logits_dtype;
   ra.bias = correction_bias;
   ra.expert_ids = expert_ids;
   ra.T = (int)T;
@@ -431,6 +467,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
     ia.E = (int)E;
     ia.F = (int)F;
     ia.K = (int)K;
+    ia.dt = c.dtype;
     ia.act = (uint16_t*)act;
     ia.y = (float*)y;
     if ((st = status_of(launch_indexed_mlp(ia, strm)))) return st;
@@ -449,6 +486,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
     g.E = (int)E;
     g.Nw = (int)(2 * F);
     g.act = 1;
+    g.act_kind = c.act.kind;
     g.layout = c.act.layout;
     g.alpha = c.act.alpha;
     g.beta = c.act.beta;
@@ -490,6 +528,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const float* log
     g.E = 1;
     g.Nw = (int)(2 * Fs);
     g.act = 1;
+    g.act_kind = MOE_ACT_SWIGLU;
     g.layout = MOE_GU_STACKED;
     g.alpha = 1.f;
     g.beta = 0.f;

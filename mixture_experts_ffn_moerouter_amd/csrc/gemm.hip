@@ -8,9 +8,11 @@
 //      applied in the epilogue and the [.., 2F] product is never written.
 // [MR] SwiGLU / [SPEC] SwiGLU Activation Function: G = min(g, limit),
 //      L = clamp(l, -limit, limit), G * sigmoid(alpha G) * (L + beta), float math,
-//      limit <= 0 disables both clamps.
+//      limit <= 0 disables both clamps. [TO] gelu_and_mul: gelu(gate) * up over stacked
+//      rows, read as the exact GELU x * Phi(x).
 //
-// bf16 kernel, templated on the tile shape: RB and CB 32-row blocks of token rows and of
+// 16-bit kernel (bfloat16 or float16 operands, the same tiles; only the MFMA and the
+// conversions differ), templated on the tile shape: RB and CB 32-row blocks of token rows and of
 // weight rows per wave, waves arranged WM x WN, so a tile is 32*RB*WM token rows x
 // 32*CB*WN weight rows, K in steps of 64 (v_mfma_f32_32x32x16_bf16, float32
 // accumulators); 128 x 128 and 128 x 256 are in use (see launch_bf16). The loop keeps
@@ -54,21 +56,31 @@ template <int RB, int CB, int BK, int NT, int WM, int NBUF>
 constexpr size_t lds_bytes() { return (size_t)NBUF * stage_elems<RB, CB, BK, NT, WM>() * 2; }
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
 
-__device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float beta,
-                                          float limit) {
-  if (limit > 0.f) {
-    g = fminf(g, limit);
-    l = fminf(fmaxf(l, -limit), limit);
-  }
-  return g * (1.0f / (1.0f + __expf(-alpha * g))) * (l + beta);
-}
 
 __device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// 32 x 32 x 16 MFMA on eight 16-bit elements per lane: DT 1 bfloat16, 2 float16.
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The gated activation of the epilogue: kind 1 gelu_and_mul, else the swiglu family.
+__device__ __forceinline__ float gated_f(int kind, float g, float l, float alpha, float beta,
+                                         float limit) {
+  return kind == 1 ? gelu_f(g) * l : swiglu_f(g, l, alpha, beta, limit);
+}
+
 template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
-          int LAYOUT, bool OUT_F32>
+          int LAYOUT, bool OUT_F32, int DT>
 __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int LDK = BK + 8, CPR = BK / 8, RSTEP = NT / CPR;  // 16-byte pieces per row
   constexpr int WN = NT / 64 / WM;  // waves: WM along the token rows x WN along the weights
@@ -213,7 +225,7 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
         for (int i = 0; i < NBW; ++i)
 #pragma unroll
           for (int j = 0; j < CB; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = mfma32<DT>(fa[i], fb[j], acc[i][j]);
       }
       if (MID >= BK / 16) mid();
     };
@@ -303,8 +315,8 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
         float bg = 0.f, bu = 0.f;
         if (bias) {
           const uint16_t* be = bias + (int64_t)e * g.Nw;
-          bg = bf16_to_f32(be[LAYOUT == 0 ? j : 2 * j]);
-          bu = bf16_to_f32(be[LAYOUT == 0 ? g.Nout + j : 2 * j + 1]);
+          bg = h16_to_f32<DT>(be[LAYOUT == 0 ? j : 2 * j]);
+          bu = h16_to_f32<DT>(be[LAYOUT == 0 ? g.Nout + j : 2 * j + 1]);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
@@ -314,10 +326,10 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
             for (int r = 0; r < 16; ++r) {
               const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
               if (m < m1) {
-                float v = swiglu_f(acc[i][h][r] + bg, acc[i][CB / 2 + h][r] + bu, g.alpha, g.beta,
-                                   g.limit);
+                float v = gated_f(g.act_kind, acc[i][h][r] + bg, acc[i][CB / 2 + h][r] + bu,
+                                  g.alpha, g.beta, g.limit);
                 if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nout + j] = v;
-                else ((uint16_t*)g.out)[(int64_t)m * g.Nout + j] = f32_to_bf16(v);
+                else ((uint16_t*)g.out)[(int64_t)m * g.Nout + j] = f32_to_h16<DT>(v);
               }
             }
           }
@@ -329,7 +341,7 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
     for (int jb = 0; jb < CB; ++jb) {
       const int n = nt * BNW + wn * 32 * CB + jb * 32 + (lane & 31);
       if (n < g.Nw) {
-        const float bn = bias ? bf16_to_f32(bias[(int64_t)e * g.Nw + n]) : 0.f;
+        const float bn = bias ? h16_to_f32<DT>(bias[(int64_t)e * g.Nw + n]) : 0.f;
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           if (i < nbw) {
@@ -340,7 +352,7 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
               if (m < m1) {
                 float v = acc[i][jb][r] + bn;
                 if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nw + n] = v;
-                else ((uint16_t*)g.out)[(int64_t)m * g.Nw + n] = f32_to_bf16(v);
+                else ((uint16_t*)g.out)[(int64_t)m * g.Nw + n] = f32_to_h16<DT>(v);
               }
             }
           }
@@ -386,7 +398,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
       sg += bias[(int64_t)e * g.Nw + rg];
       su += bias[(int64_t)e * g.Nw + ru];
     }
-    ((float*)g.out)[(int64_t)m * g.Nout + n] = swiglu_f(sg, su, g.alpha, g.beta, g.limit);
+    ((float*)g.out)[(int64_t)m * g.Nout + n] = gated_f(g.act_kind, sg, su, g.alpha, g.beta, g.limit);
   } else {
     float s = 0.f;
     for (int k = 0; k < g.Kd; ++k) s = fmaf(srow[k], B[(int64_t)n * g.Kd + k], s);
@@ -396,14 +408,14 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
-          int LAYOUT, bool OUT_F32>
+          int LAYOUT, bool OUT_F32, int DT>
 hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
   constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * (NT / 64 / WM);
   const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
   const int64_t max_tiles = (g.M + BMX - 1) / BMX + (g.E < g.M ? g.E : g.M);
   int64_t grid = max_tiles * n_tiles_n;
   grid = (grid + kXcd - 1) / kXcd * kXcd;
-  const auto kern = gemm_bf16_kernel<RB, CB, PA, BK, NT, WM, OCC, MID, NBUF, ACT, LAYOUT, OUT_F32>;
+  const auto kern = gemm_bf16_kernel<RB, CB, PA, BK, NT, WM, OCC, MID, NBUF, ACT, LAYOUT, OUT_F32, DT>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes<RB, CB, BK, NT, WM, NBUF>());
@@ -419,12 +431,25 @@ hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
 // workgroup's prologue and epilogue overlap the other's K loop. Both keep the two
 // operands two K steps ahead. Measured in one process, alternating the shapes: 5% and 3%
 // faster layers with the wide tile at Kd 7168 and 2880, 2% slower at Kd 2048 / 768.
-template <bool ACT, int LAYOUT, bool OUT_F32>
+template <bool ACT, int LAYOUT, bool OUT_F32, int DT>
 hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
   // <RB, CB, PA, BK, NT, WM, OCC, MID, NBUF>
   if (g.Kd >= 2560)
-    return launch_bf16_shape<2, 2, 2, 64, 512, 2, 1, 4, 2, ACT, LAYOUT, OUT_F32>(g, s);
-  return launch_bf16_shape<2, 2, 2, 64, 256, 2, 2, 4, 2, ACT, LAYOUT, OUT_F32>(g, s);
+    return launch_bf16_shape<2, 2, 2, 64, 512, 2, 1, 4, 2, ACT, LAYOUT, OUT_F32, DT>(g, s);
+  return launch_bf16_shape<2, 2, 2, 64, 256, 2, 2, 4, 2, ACT, LAYOUT, OUT_F32, DT>(g, s);
+}
+
+template <int DT>
+hipError_t launch_h16(const GemmArgs& g, hipStream_t s) {
+  if (g.act) {
+    if (g.layout == 0)
+      return g.out_dt == 0 ? launch_bf16<true, 0, true, DT>(g, s)
+                           : launch_bf16<true, 0, false, DT>(g, s);
+    return g.out_dt == 0 ? launch_bf16<true, 1, true, DT>(g, s)
+                         : launch_bf16<true, 1, false, DT>(g, s);
+  }
+  return g.out_dt == 0 ? launch_bf16<false, 0, true, DT>(g, s)
+                       : launch_bf16<false, 0, false, DT>(g, s);
 }
 
 }  // namespace
@@ -436,15 +461,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s) {
     gemm_f32_kernel<<<grid, 256, (size_t)g.Kd * sizeof(float), s>>>(g);
     return hipGetLastError();
   }
-  if (g.act) {
-    if (g.layout == 0)
-      return g.out_dt == 0 ? launch_bf16<true, 0, true>(g, s)
-                           : launch_bf16<true, 0, false>(g, s);
-    return g.out_dt == 0 ? launch_bf16<true, 1, true>(g, s)
-                         : launch_bf16<true, 1, false>(g, s);
-  }
-  return g.out_dt == 0 ? launch_bf16<false, 0, true>(g, s)
-                       : launch_bf16<false, 0, false>(g, s);
+  return g.dt == 2 ? launch_h16<2>(g, s) : launch_h16<1>(g, s);
 }
 
 }  // namespace moe

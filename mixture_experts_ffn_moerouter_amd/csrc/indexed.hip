@@ -22,7 +22,8 @@
 // Inside a block the contraction order is permuted identically for both operands
 // (MFMA u, lane quarter q takes the 8 elements of piece 4u + q), so the sums are those
 // of the plain dot products up to float32 rounding order.
-//   gate_up: act[route, j] = silu(h W_g[j]) * (h W_u[j]), rounded to bf16 (workspace)
+//   gate_up: act[route, j] = silu(h W_g[j]) * (h W_u[j]), rounded to the operand dtype
+//            (bfloat16 or float16; the MFMA follows the dtype) (workspace)
 //   down:    y[route, n]   = act[route] . W_d[n], float32 (workspace); the combine
 //            kernel then sums the routes of each token.
 #include "moe_internal.h"
@@ -43,10 +44,22 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * (1.0f / (1.0f + __expf(-g))) * u;
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+
+// 16 x 16 x 32 MFMA on eight 16-bit elements per lane: DT 1 bfloat16, 2 float16.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // One wave: rows row_g[0] + [0,16) and row_g[1] + [0,16) of the expert's weight matrix
 // w (rows of Kd elements) against the routes [c0, c0 + 16) of the expert, over the full
 // contraction. acc[g] receives D[i][c] (lane: route c = lane % 16, rows 4*(lane/16)+r).
-template <bool GATE_UP>
+template <bool GATE_UP, int DT>
 __device__ __forceinline__ void stream_rows(const IndexedArgs& p, bf16x8 (*stage)[16],
                                             __amdgpu_buffer_rsrc_t rw, const int* row_g,
                                             int Kd, int c0, int o1, f32x4* acc) {
@@ -103,7 +116,7 @@ __device__ __forceinline__ void stream_rows(const IndexedArgs& p, bf16x8 (*stage
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int g = 0; g < 2; ++g)
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f[g][u], x[u], acc[g], 0, 0, 0);
+        acc[g] = mfma16<DT>(f[g][u], x[u], acc[g]);
   };
 
   issue(0, w0, x0);
@@ -124,7 +137,7 @@ __device__ __forceinline__ void stream_rows(const IndexedArgs& p, bf16x8 (*stage
 
 // Work items per expert: gate_up F/16 (16 act columns each), down H/32 (32 hidden rows);
 // each workgroup takes kWaves consecutive items of one expert.
-template <bool GATE_UP>
+template <bool GATE_UP, int DT>
 __global__ __launch_bounds__(64 * kWaves, 2) void indexed_kernel(IndexedArgs p) {
   __shared__ bf16x8 stage_all[kWaves][32][16];
   const int items = GATE_UP ? p.F / 16 : p.H / 32;
@@ -154,14 +167,14 @@ __global__ __launch_bounds__(64 * kWaves, 2) void indexed_kernel(IndexedArgs p) 
   const int c = lane & 15, q = lane >> 4;
   for (int c0 = o0; c0 < o1; c0 += 16) {
     f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-    stream_rows<GATE_UP>(p, stage_all[wave], rw, row_g, Kd, c0, o1, acc);
+    stream_rows<GATE_UP, DT>(p, stage_all[wave], rw, row_g, Kd, c0, o1, acc);
     const int s = c0 + c;
     if (s < o1) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 4 * q + r;
         if (GATE_UP)
-          p.act[(int64_t)s * F + item * 16 + i] = f32_to_bf16(silu_mul(acc[0][r], acc[1][r]));
+          p.act[(int64_t)s * F + item * 16 + i] = f32_to_h16<DT>(silu_mul(acc[0][r], acc[1][r]));
         else {
           p.y[(int64_t)s * H + item * 32 + i] = acc[0][r];
           p.y[(int64_t)s * H + item * 32 + 16 + i] = acc[1][r];
@@ -173,15 +186,20 @@ __global__ __launch_bounds__(64 * kWaves, 2) void indexed_kernel(IndexedArgs p) 
 
 }  // namespace
 
+template <int DT>
+hipError_t launch_indexed_dt(const IndexedArgs& a, int max_active, hipStream_t s) {
+  indexed_kernel<true, DT><<<dim3(max_active * (a.F / 16 / kWaves)), 64 * kWaves, 0, s>>>(a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  indexed_kernel<false, DT><<<dim3(max_active * (a.H / 32 / kWaves)), 64 * kWaves, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 hipError_t launch_indexed_mlp(const IndexedArgs& a, hipStream_t s) {
   const int R = a.T * a.K;
   const int max_active = R < a.E ? R : a.E;
   if (max_active <= 0) return hipSuccess;
-  indexed_kernel<true><<<dim3(max_active * (a.F / 16 / kWaves)), 64 * kWaves, 0, s>>>(a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  indexed_kernel<false><<<dim3(max_active * (a.H / 32 / kWaves)), 64 * kWaves, 0, s>>>(a);
-  return hipGetLastError();
+  return a.dt == 2 ? launch_indexed_dt<2>(a, max_active, s) : launch_indexed_dt<1>(a, max_active, s);
 }
 
 }  // namespace moe

@@ -26,6 +26,39 @@ __device__ __forceinline__ uint16_t f32_to_f16(float f) {
   _Float16 h = (_Float16)f;  // round to nearest even
   return __builtin_bit_cast(uint16_t, h);
 }
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// 16-bit operand types by dtype code: 1 bfloat16, 2 float16.
+template <int DT> __device__ __forceinline__ float h16_to_f32(uint16_t h) {
+  return DT == 2 ? f16_to_f32(h) : bf16_to_f32(h);
+}
+template <int DT> __device__ __forceinline__ uint16_t f32_to_h16(float f) {
+  return DT == 2 ? f32_to_f16(f) : f32_to_bf16(f);
+}
+// Load one element of dtype `dt` (0 f32, 1 bf16, 2 f16) as float32.
+__device__ __forceinline__ float load_dt(const void* p, int dt, int64_t i) {
+  if (dt == 0) return ((const float*)p)[i];
+  const uint16_t h = ((const uint16_t*)p)[i];
+  return dt == 1 ? bf16_to_f32(h) : f16_to_f32(h);
+}
+
+// [MR] SwiGLU / [SPEC] SwiGLU Activation Function, float32: G = min(g, limit),
+// L = clamp(l, -limit, limit), G * sigmoid(alpha G) * (L + beta); limit <= 0 disables
+// both clamps.
+__device__ __forceinline__ float swiglu_f(float g, float l, float alpha, float beta,
+                                          float limit) {
+  if (limit > 0.f) {
+    g = fminf(g, limit);
+    l = fminf(fmaxf(l, -limit), limit);
+  }
+  return g * (1.0f / (1.0f + __expf(-alpha * g))) * (l + beta);
+}
+
+// Exact GELU, x * Phi(x) = x (1 + erf(x / sqrt 2)) / 2, float32.
+__device__ __forceinline__ float gelu_f(float x) {
+  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+}
 
 // Store one float32 value in dtype `dt` (0 f32, 1 bf16, 2 f16) at element i of p.
 __device__ __forceinline__ void store_dt(void* p, int dt, int64_t i, float v) {
@@ -39,7 +72,8 @@ __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __ex
 // ------------------------------------------------------------------ launchers
 // Each returns a hipError_t; arguments are validated by the caller (api.hip).
 struct RouteArgs {
-  const float* logits;
+  const void* logits;     // [T, E] in logits_dt
+  int logits_dt;          // 0 f32, 1 bf16, 2 f16
   const float* bias;
   const int32_t* expert_ids;
   int T, E, K, scoring, renormalize, G, TG;
@@ -73,6 +107,7 @@ struct GemmArgs {
   const int32_t* offsets;
   int E, Nw;          // weight rows per expert
   int act;            // 0 none, 1 gated activation
+  int act_kind;       // 0 swiglu family (alpha, beta, limit), 1 gelu_and_mul
   int layout;         // moe_gu_layout when act
   float alpha, beta, limit;
   void* out;          // [M, Nout]
@@ -85,7 +120,7 @@ hipError_t launch_combine(const void* y, int y_dt, const float* w, const int32_t
                           int T, int K, int H, float scale, void* out, int out_dt,
                           hipStream_t s);
 
-// Indexed small-route backend (bf16, silu_and_mul, no bias).
+// Indexed small-route backend (bf16 or f16, silu_and_mul, no bias).
 struct IndexedArgs {
   const uint16_t* hidden;     // [T, H]
   const int32_t* sorted_route;
@@ -94,6 +129,7 @@ struct IndexedArgs {
   const uint16_t* w_gate_up;  // [E, 2F, H] stacked
   const uint16_t* w_down;     // [E, H, F]
   int T, H, E, F, K;
+  int dt;                     // 1 bf16, 2 f16
   uint16_t* act;              // [R, F] workspace (permuted rows)
   float* y;                   // [R, H] workspace (permuted rows)
 };
@@ -110,5 +146,18 @@ struct Fp8GemmArgs {
   uint16_t* out;          // [E, max_m, N] bf16
 };
 hipError_t launch_gemm_fp8_masked(const Fp8GemmArgs& g, hipStream_t s);
+
+// Standalone gated activation: out[r, j] = act(gate[r, j], up[r, j]) over rows x F.
+struct SwigluArgs {
+  const void* gate;   // [rows, F] (up given) or [rows, 2F] (fused)
+  const void* up;     // [rows, F] or null
+  int64_t rows;
+  int F;
+  int fusion;         // up null: 0 stacked (gate then up), 1 interleaved
+  int dt;             // 0 f32, 1 bf16, 2 f16 (inputs and output)
+  float alpha, beta, limit;
+  void* out;          // [rows, F]
+};
+hipError_t launch_swiglu(const SwigluArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
   const int t = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
   if (t >= p.T) return;  // uniform per wave
   const int E = p.E;
-  const float* z = p.logits + (int64_t)t * E;
+  const int64_t z0 = (int64_t)t * E;
 
   float s[PL], u[PL];
   bool valid[PL];
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
   for (int j = 0; j < PL; ++j) {
     int e = lane + 64 * j;
     valid[j] = e < E;
-    s[j] = valid[j] ? z[e] : -INFINITY;
+    s[j] = valid[j] ? load_dt(p.logits, p.logits_dt, z0 + e) : -INFINITY;
   }
   // ---- scoring, float32
   if (p.scoring == 0) {  // softmax over all E experts

@@ -145,6 +145,7 @@ class MoEConfig:
     router_probs_dtype: Optional[str] = None
     hash_routing: bool = False
     logit_skew: float = 0.0                     # logits[:, e] += logit_skew * e / (E - 1)
+    logits_dtype: str = "f32"                   # storage of the router logits
     notes: str = field(default="", compare=False)
 
     @property
@@ -177,6 +178,11 @@ CONFIGS = {
     # Skewed expert load (a per-expert logit offset): a few experts take most tokens.
     "qwen3_skewed_bf16": MoEConfig("qwen3_skewed_bf16", T=4096, H=2048, E=128, F=768, K=8,
                                    logit_skew=6.0),
+    # The Qwen3 shapes with float16 operands, and with gelu_and_mul (the next rows' dtype
+    # and activation on the bench workload's shapes).
+    "qwen3_f16": MoEConfig("qwen3_f16", T=4096, H=2048, E=128, F=768, K=8, dtype="f16"),
+    "qwen3_gelu_bf16": MoEConfig("qwen3_gelu_bf16", T=4096, H=2048, E=128, F=768, K=8,
+                                 act="gelu_and_mul"),
     "decode_dsv3_bf16": MoEConfig("decode_dsv3_bf16", T=16, H=7168, E=256, F=2048, K=8,
                                   scoring="sigmoid", rsf=2.5, G=8, TG=4,
                                   correction_bias=(-0.1, 0.1)),
@@ -184,6 +190,11 @@ CONFIGS = {
     "router_ep_f16": MoEConfig("router_ep_f16", T=16, H=0, E=256, F=0, K=8,
                                scoring="sqrt_softplus", local_expert_start=64,
                                local_expert_count=64, router_probs_dtype="f16"),
+    # Router-only pass at prefill size with bfloat16 logits: the DeepSeek-V3 router
+    # (sigmoid, correction bias, 8 groups / 4 kept, top-8, scaling 2.5).
+    "router_dsv3_bf16_logits": MoEConfig("router_dsv3_bf16_logits", T=4096, H=0, E=256, F=0,
+                                         K=8, scoring="sigmoid", rsf=2.5, G=8, TG=4,
+                                         correction_bias=(-0.1, 0.1), logits_dtype="bf16"),
 }
 
 
@@ -200,6 +211,8 @@ def make_router_inputs(cfg: MoEConfig, *, seed: int = 0, device="cpu") -> dict:
                                        dtype=torch.float32, device=device)
     if cfg.hash_routing:
         d["expert_ids"] = random_expert_ids(cfg.T, cfg.K, cfg.E, seed=seed, device=device)
+    if cfg.logits_dtype != "f32":
+        d["logits"] = d["logits"].to(_TORCH_DT[cfg.logits_dtype])
     return d
 
 

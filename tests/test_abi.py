@@ -24,7 +24,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(B.SYMBOLS)
     L = B.lib()
     for n in names:
@@ -33,16 +33,33 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = B.lib()
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == B.ABI_VERSION == 2
     texts = {L.moe_status_str(s).decode() for s in range(6)}
     assert len(texts) == 6
     assert L.moe_status_str(99).decode() == "unknown status"
 
 
-def test_struct_sizes_match_header():
-    assert ctypes.sizeof(B.MoeRouteCfg) == 36
-    assert ctypes.sizeof(B.MoeActCfg) == 16
-    assert ctypes.sizeof(B.MoeFfnCfg) == 104
+def test_struct_layout_matches_header(tmp_path):
+    """Sizes and field offsets of the binding's ctypes structs against the C header,
+    compiled here with the host compiler."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    fields = {"moe_route_cfg": B.MoeRouteCfg, "moe_act_cfg": B.MoeActCfg,
+              "moe_ffn_cfg": B.MoeFfnCfg}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', 'int main(void) {']
+    for cname, ct in fields.items():
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in ct._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ['  return 0;', '}']
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)], text=True).splitlines())
+    for cname, ct in fields.items():
+        assert int(got[cname]) == ctypes.sizeof(ct), cname
+        for f, _ in ct._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(ct, f).offset, (cname, f)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "qwen3_bf16", "gptoss_bf16", "dsv3_bf16",
@@ -51,12 +68,12 @@ def test_backend_choice_follows_dispatch_rule(name):
     cfg = I.CONFIGS[name]
     has_bias = cfg.bias_std is not None
     want_indexed = O.indexed_backend_applies(cfg.T, cfg.K, cfg.E, cfg.H, cfg.F, cfg.act,
-                                             has_bias) and cfg.dtype == "bf16"
+                                             has_bias) and cfg.dtype in ("bf16", "f16")
     got = B.moe_ffn_backend(B.ffn_cfg(cfg), has_bias)
     assert got == (2 if want_indexed else 1)
     assert B.moe_ffn_backend(B.ffn_cfg(cfg, "staged"), has_bias) == 1
     forced = B.moe_ffn_backend(B.ffn_cfg(cfg, "indexed"), has_bias)
-    assert forced == (2 if (cfg.dtype == "bf16" and not has_bias and cfg.act == "silu_and_mul"
+    assert forced == (2 if (cfg.dtype in ("bf16", "f16") and not has_bias and cfg.act == "silu_and_mul"
                             and cfg.H % 128 == 0 and cfg.F % 256 == 0) else -1)
 
 
@@ -159,9 +176,15 @@ def test_ffn_argument_errors():
     c = list(a)
     c[11] = FAKE + (1 << 41)      # shared_out without a shared expert
     assert ffn(cfg, c) == B.MOE_ERR_INVALID_ARG
-    f16 = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
-    f16.dtype = 2
-    assert ffn(f16, a) == B.MOE_ERR_UNSUPPORTED
+    bad_dt = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
+    bad_dt.dtype = 3
+    assert ffn(bad_dt, a) == B.MOE_ERR_UNSUPPORTED
+    gelu_il = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
+    gelu_il.act.kind, gelu_il.act.layout = 1, 1   # gelu_and_mul is stacked only
+    assert ffn(gelu_il, a) == B.MOE_ERR_INVALID_ARG
+    bad_logits = B.ffn_cfg(I.CONFIGS["tiny_fp32"])
+    bad_logits.route.logits_dtype = 7
+    assert ffn(bad_logits, a) == B.MOE_ERR_INVALID_ARG
     forced = B.ffn_cfg(I.CONFIGS["tiny_fp32"], "indexed")
     assert ffn(forced, a) == B.MOE_ERR_UNSUPPORTED
 
@@ -183,3 +206,29 @@ def test_fp8_masked_gemm_argument_errors():
     assert f(out=A + 64) == B.MOE_ERR_OVERLAP         # out over a
     assert f(out=C) == B.MOE_ERR_OVERLAP              # out over counts
     assert f(m=0, a=None, sa=None, out=None) == B.MOE_OK  # nothing to do, nothing launched
+
+
+def test_route_logits_dtype_errors():
+    cfg = B.route_cfg(2)
+    cfg.logits_dtype = 5
+    assert _route(cfg=cfg) == B.MOE_ERR_INVALID_ARG
+    # 16-bit logits: a T*E*2-byte input; weights placed inside it overlap
+    cfg16 = B.route_cfg(2)
+    cfg16.logits_dtype = 1
+    assert _route(T=4, E=8, cfg=cfg16, w=FAKE + 48) == B.MOE_ERR_OVERLAP
+
+
+def test_swiglu_argument_errors():
+    L = B.lib()
+    G, U, OUT = FAKE, FAKE + (1 << 30), FAKE + (1 << 31)
+    f = lambda g=G, u=U, rows=16, F=64, dt=1, fusion=0, out=OUT: L.moe_swiglu(
+        g, u, rows, F, dt, fusion, 1.0, 0.0, 0.0, out, None)
+    assert f(g=None) == B.MOE_ERR_INVALID_ARG
+    assert f(out=None) == B.MOE_ERR_INVALID_ARG
+    assert f(F=0) == B.MOE_ERR_INVALID_ARG
+    assert f(rows=-1) == B.MOE_ERR_INVALID_ARG
+    assert f(u=None, fusion=2) == B.MOE_ERR_INVALID_ARG
+    assert f(dt=4) == B.MOE_ERR_UNSUPPORTED
+    assert f(out=U + 100) == B.MOE_ERR_OVERLAP               # out over up
+    assert f(u=None, out=G + 16 * 64 * 2 + 2) == B.MOE_ERR_OVERLAP  # inside fused [16, 128]
+    assert f(rows=0, g=None, u=None, out=None) == B.MOE_OK

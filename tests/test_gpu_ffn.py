@@ -35,6 +35,23 @@ SMALL = {
     "single_token": I.MoEConfig("single_token", T=1, H=128, E=4, F=64, K=2),
     # a per-expert logit ramp: some experts take most tokens, many take none
     "skewed_load": I.MoEConfig("skewed_load", T=600, H=320, E=48, F=192, K=6, logit_skew=6.0),
+    # float16 operands (staged and indexed), gelu_and_mul, 16-bit router logits
+    "qwen_like_f16": I.MoEConfig("qwen_like_f16", T=300, H=256, E=16, F=192, K=4, dtype="f16"),
+    "gptoss_like_f16": I.MoEConfig("gptoss_like_f16", T=200, H=200, E=8, F=96, K=4,
+                                   act="swigluoai", bias_std=0.3, x_std=4.0, w_std=0.1,
+                                   dtype="f16"),
+    "decode_like_indexed_f16": I.MoEConfig("decode_like_indexed_f16", T=16, H=256, E=64,
+                                           F=256, K=4, scoring="sigmoid", G=4, TG=2,
+                                           correction_bias=(-0.1, 0.1), rsf=2.5, dtype="f16"),
+    "gelu_like": I.MoEConfig("gelu_like", T=300, H=256, E=16, F=192, K=4, act="gelu_and_mul",
+                             x_std=2.0, w_std=0.1),
+    "gelu_like_f32": I.MoEConfig("gelu_like_f32", T=70, H=96, E=12, F=40, K=3, dtype="f32",
+                                 act="gelu_and_mul", bias_std=0.1, w_std=0.1),
+    "bf16_logits_groups": I.MoEConfig("bf16_logits_groups", T=256, H=512, E=32, F=128, K=8,
+                                      scoring="sigmoid", rsf=2.5, G=8, TG=4,
+                                      correction_bias=(-0.1, 0.1), logits_dtype="bf16"),
+    "f16_logits_softmax": I.MoEConfig("f16_logits_softmax", T=300, H=256, E=16, F=192, K=4,
+                                      logits_dtype="f16"),
 }
 
 
@@ -91,7 +108,7 @@ def test_ffn_small(name):
         assert B.moe_ffn_backend(B.ffn_cfg(cfg), False) == 2
         out_s, _ = run_gpu(cfg, d, "staged")
         torch.cuda.synchronize()
-        assert_close(np64(out_s), np64(out), "bf16", "indexed vs staged")
+        assert_close(np64(out_s), np64(out), cfg.dtype, "indexed vs staged")
 
 
 def test_indexed_passes_over_route_groups():
@@ -129,9 +146,10 @@ def test_ffn_zero_tokens():
 
 # Full-size workloads: every output computed on the GPU, sampled tokens checked.
 FULL = ["tiny_fp32", "qwen3_bf16", "gptoss_bf16", "dsv3_bf16", "decode_dsv3_bf16",
-        "qwen3_skewed_bf16"]
+        "qwen3_skewed_bf16", "qwen3_f16", "qwen3_gelu_bf16"]
 SAMPLES = {"tiny_fp32": 64, "qwen3_bf16": 12, "gptoss_bf16": 8, "dsv3_bf16": 4,
-           "decode_dsv3_bf16": 6, "qwen3_skewed_bf16": 8}
+           "decode_dsv3_bf16": 6, "qwen3_skewed_bf16": 8, "qwen3_f16": 12,
+           "qwen3_gelu_bf16": 12}
 
 
 @pytest.mark.parametrize("name", FULL)

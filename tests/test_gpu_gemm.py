@@ -8,7 +8,7 @@ from mixture_experts_ffn_moerouter_amd import binding as B
 from moe_testlib import assert_close, guarded, np64, say
 
 pytestmark = pytest.mark.gpu
-DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def _offsets(sizes):
@@ -24,7 +24,7 @@ SEGMENTS = {
 }
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("seg", sorted(SEGMENTS))
 # (K, N); K >= 2560 takes the wide 128 x 256 tile, with a ragged K tail here
 @pytest.mark.parametrize("shape", [(256, 384), (200, 136), (72, 40), (2600, 300)])
@@ -39,7 +39,7 @@ def test_grouped_gemm(dt, seg, shape, bias):
     b = (0.1 * torch.randn((E, N, Kd), device="cuda", generator=g)).to(DT[dt])
     bb = (0.1 * torch.randn((E, N), device="cuda", generator=g)).to(DT[dt]) if bias else None
     off = _offsets(sizes)
-    for out_dt in ([DT[dt], torch.float32] if dt == "bf16" else [torch.float32]):
+    for out_dt in ([DT[dt], torch.float32] if dt != "f32" else [torch.float32]):
         out, check = guarded((M, N), out_dt)
         B.moe_grouped_gemm(a, b, off, bb, out_dtype=out_dt, out=out)
         torch.cuda.synchronize()
@@ -51,12 +51,12 @@ def test_grouped_gemm(dt, seg, shape, bias):
         assert_close(np64(out), ref, "f32" if out_dt == torch.float32 else dt, f"gemm {seg}")
 
 
-ACTS = {"silu_and_mul": "silu_and_mul", "swigluoai": "swigluoai",
+ACTS = {"silu_and_mul": "silu_and_mul", "swigluoai": "swigluoai", "gelu_and_mul": "gelu_and_mul",
         "custom_clamped": ("stacked", 1.3, 0.25, 2.0),
         "interleaved_noclamp": ("interleaved", 0.8, -0.5, 0.0)}
 
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 @pytest.mark.parametrize("seg", ["ragged", "uniform256"])
 @pytest.mark.parametrize("act", sorted(ACTS))
 @pytest.mark.parametrize("gather", [False, True])

@@ -119,3 +119,24 @@ def test_route_deterministic():
     b = B.moe_route(logits, cfg, cb)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("ldt", ["bf16", "f16"])
+@pytest.mark.parametrize("scoring,groups", [("softmax", (1, 1)), ("sigmoid", (8, 4)),
+                                            ("sqrt_softplus", (1, 1))])
+def test_route_16bit_logits(ldt, scoring, groups):
+    """bfloat16 / float16 logits ([TO] FusedTopKFwdOp): each value is read exactly into
+    float32, so the result is the oracle's on the same (exactly widened) values."""
+    G, TG = groups
+    T, E, K = 1000, 256, 8
+    say(f"[route] {ldt} logits, {scoring}, groups {groups}")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    logits = (2.0 * torch.randn((T, E), device="cuda", generator=g)).to(
+        {"bf16": torch.bfloat16, "f16": torch.float16}[ldt])
+    bias = (0.1 * torch.rand((E,), device="cuda", generator=g)) if scoring == "sigmoid" else None
+    cfg = B.route_cfg(K, scoring, True, 2.5 if scoring == "sigmoid" else 1.0, G, TG)
+    w, ids, _, _ = B.moe_route(logits, cfg, bias)
+    torch.cuda.synchronize()
+    r = O.route(np64(logits), K, scoring, True, 2.5 if scoring == "sigmoid" else 1.0, G, TG,
+                None if bias is None else np64(bias))
+    check_route(w, ids, r, f"{ldt} {scoring}")
