@@ -44,9 +44,9 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 TRAFFIC = {
     # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
     # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE).
-    # gate_up: 528790.5 + 49152.9 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1133268249,
-                   "gemm_src": "19afab5a2e42ccf7c0d5a33d7016ddd43f3a8e506bba2c1fe7caafc8aa735301"},
+    # gate_up: 528831.5 + 49153.1 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1133352419,
+                   "gemm_src": "d615652da72a0f9aeb93fc93a77398799f61b66ed69f8639e5041dfdf29e6472"},
     # 4512238.0 + 263745.7 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9510906364,
                          "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
@@ -196,8 +196,9 @@ def router_line(cfg, args):
                        cfg.local_expert_start, cfg.local_expert_count or 0,
                        cfg.router_probs_dtype or "f32")
     stream = torch.cuda.current_stream()
+    ep = cfg.local_expert_count is not None
     call = lambda: B.moe_route(d["logits"], rcfg, d.get("correction_bias"),
-                               d.get("expert_ids"), with_router_probs=True, stream=stream)
+                               d.get("expert_ids"), with_router_probs=ep, stream=stream)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -208,8 +209,9 @@ def router_line(cfg, args):
     ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
     k_ms = time_launches(call, args.kernel_reps, stream)
     rp = 2 if cfg.router_probs_dtype in ("f16", "bf16") else 4
-    k_bytes = cfg.T * cfg.E * 4 + (cfg.E * 4 if cfg.correction_bias else 0) \
-        + cfg.T * cfg.K * 8 + cfg.T * (cfg.local_expert_count or 0) * rp + cfg.T * rp
+    lg = 2 if cfg.logits_dtype in ("f16", "bf16") else 4
+    k_bytes = cfg.T * cfg.E * lg + (cfg.E * 4 if cfg.correction_bias else 0) \
+        + cfg.T * cfg.K * 8 + ((cfg.local_expert_count + 1) * cfg.T * rp if ep else 0)
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s",
@@ -218,15 +220,94 @@ def router_line(cfg, args):
         "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded SplitMix64/Box-Muller logits)",
         "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "top_k": cfg.K,
-                   "scoring": cfg.scoring, "local_expert_start": cfg.local_expert_start,
+                   "scoring": cfg.scoring, "logits_dtype": cfg.logits_dtype,
+                   "num_expert_group": cfg.G, "topk_group": cfg.TG,
+                   "local_expert_start": cfg.local_expert_start,
                    "local_expert_count": cfg.local_expert_count,
                    "router_probs_dtype": cfg.router_probs_dtype, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
-                     "traffic": None, "kernel": "route_kernel (launch-bound: tiny input)",
+                     "traffic": None,
+                     "kernel": "route_kernel" + (" (launch-bound: tiny input)" if cfg.T <= 64 else ""),
                      "kernel_ms": round(k_ms, 5), "latency_us": round(k_ms * 1e3, 2),
                      "algorithmic_bytes": k_bytes},
     }
+    if not args.no_cpu_baseline:
+        import oracle.moe_oracle as O
+        threads = _blas_threads()
+        logits = d["logits"].float().cpu().numpy().astype(np.float64)
+        bias = None if d.get("correction_bias") is None else \
+            d["correction_bias"].cpu().numpy().astype(np.float64)
+        done, total = 0, 0.0
+        n = min(cfg.T, 256)
+        while total < args.cpu_budget / 4:
+            t1 = time.perf_counter()
+            O.route(logits[:n], cfg.K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG,
+                    bias)
+            total += time.perf_counter() - t1
+            done += n
+        line["cpu_baseline"] = {"value": done / total, "unit": "tokens/s", "cores": threads,
+                                "kind": "oracle",
+                                "sample": f"first {n} of {cfg.T} tokens, repeated "
+                                          f"({done} routed), float64 numpy oracle, {total:.1f} s"}
+    print(json.dumps(line), flush=True)
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] + [1]))
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def swiglu_line(cfg, args):
+    """Standalone SwiGLU operator: one call per step over [rows, 2F] -> [rows, F]; value =
+    rows per second; roofline against HBM over the bytes the op must move."""
+    d = I.make_swiglu_inputs(cfg, device="cuda")
+    out = torch.empty((cfg.rows, cfg.F), dtype=d["gate"].dtype, device="cuda")
+    stream = torch.cuda.current_stream()
+    call = lambda: B.moe_swiglu(d["gate"], None, cfg.alpha, cfg.beta, cfg.limit, cfg.fusion,
+                                out=out, stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    k_ms = time_launches(call, args.kernel_reps, stream)
+    es = 4 if cfg.dtype == "f32" else 2
+    k_bytes = cfg.rows * cfg.F * 3 * es
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(cfg.rows / (ms_per_step * 1e-3), 1), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype + " storage, f32 arithmetic",
+        "data": "synthetic (seeded SplitMix64/Box-Muller values)",
+        "config": {"workload": cfg.name, "rows": cfg.rows, "F": cfg.F, "fusion": cfg.fusion,
+                   "alpha": cfg.alpha, "beta": cfg.beta, "limit": cfg.limit,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "swiglu_vec_kernel (standalone SwiGLU)",
+                     "kernel_ms": round(k_ms, 5), "algorithmic_bytes": k_bytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.moe_oracle as O
+        x = d["gate"][:512].float().cpu().numpy().astype(np.float64)
+        done, total = 0, 0.0
+        while total < args.cpu_budget / 4:
+            t1 = time.perf_counter()
+            O.swiglu_op(x, None, cfg.alpha, cfg.beta, cfg.limit, cfg.fusion, cfg.dtype)
+            total += time.perf_counter() - t1
+            done += x.shape[0]
+        line["cpu_baseline"] = {"value": done / total, "unit": "rows/s",
+                                "cores": _blas_threads(), "kind": "oracle",
+                                "sample": f"first 512 of {cfg.rows} rows, repeated ({done} "
+                                          f"rows), float64 numpy oracle, {total:.1f} s"}
     print(json.dumps(line), flush=True)
 
 
@@ -352,7 +433,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_bf16",
-                    choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS))
+                    choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS) + sorted(I.SWIGLU_CONFIGS))
     ap.add_argument("--backend", default="auto", choices=["auto", "staged", "indexed"])
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -371,6 +452,10 @@ def main():
     if args.workload in I.FP8_CONFIGS:
         torch.cuda.set_device(0)
         fp8_line(I.FP8_CONFIGS[args.workload], args)
+        return
+    if args.workload in I.SWIGLU_CONFIGS:
+        torch.cuda.set_device(0)
+        swiglu_line(I.SWIGLU_CONFIGS[args.workload], args)
         return
     cfg = I.CONFIGS[args.workload]
     if cfg.H == 0:

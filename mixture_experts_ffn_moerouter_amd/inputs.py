@@ -313,3 +313,36 @@ def fp8_counts(cfg: Fp8GemmConfig, *, seed: int = 0, device="cpu") -> torch.Tens
     c = normal((cfg.E,), cfg.rows_std, seed=seed, stream=STREAMS["fp8_counts"],
                dtype=torch.float64, device=device, mean=cfg.rows_mean)
     return c.round().clamp(0, cfg.max_m).to(torch.int32)
+
+
+# --------------------------------------------------------------------------------------
+# Standalone SwiGLU operator ([MR] SwiGLU): one fused [rows, 2F] projection in, [rows, F]
+# out.
+
+@dataclass(frozen=True)
+class SwigluConfig:
+    name: str
+    rows: int
+    F: int
+    dtype: str = "bf16"
+    fusion: str = "stacked"        # gate then up ([MR], up omitted)
+    alpha: float = 1.702
+    beta: float = 1.0
+    limit: float = 7.0
+    x_std: float = 4.0             # the clamps fire at |x| > 7
+
+
+SWIGLU_CONFIGS = {
+    # The [MR] case: a tensor-parallel shared expert's fused gate_up output (16384 tokens x
+    # 2 x 4096), the gpt-oss constants.
+    "swiglu_bf16": SwigluConfig("swiglu_bf16", rows=16384, F=4096),
+    "swiglu_small": SwigluConfig("swiglu_small", rows=37, F=96, dtype="f16",
+                                 fusion="interleaved"),
+}
+
+
+def make_swiglu_inputs(cfg: SwigluConfig, *, seed: int = 0, device="cpu") -> dict:
+    """The fused projection: STREAMS["hidden"] values at x_std, [rows, 2F]."""
+    return {"gate": normal((cfg.rows, 2 * cfg.F), cfg.x_std, seed=seed,
+                           stream=STREAMS["hidden"], dtype=_TORCH_DT[cfg.dtype],
+                           device=device)}
