@@ -36,7 +36,8 @@ __all__ = [
     "routing_weights", "ep_router_outputs", "RouteResult", "route", "swiglu", "gelu",
     "gated", "swiglu_op", "ACTIVATIONS", "split_gate_up", "expert_mlp", "grouped_gemm",
     "grouped_gemm_act",
-    "permute", "combine", "shared_expert_mlp", "moe_ffn_forward",
+    "permute", "combine", "permute_align", "pre_permute", "grouped_gemm_layout",
+    "shared_expert_mlp", "moe_ffn_forward",
     "indexed_backend_applies", "decode_e4m3fn", "grouped_gemm_fp8_masked", "PARITY_STATUS",
 ]
 
@@ -413,16 +414,143 @@ def combine(y, topk_weights, route_pos, scale: float = 1.0, out_dtype: str = "f3
     """out[t] = scale * sum_k topk_weights[t,k] * y[route_pos[t*K + k]], k ascending.
 
     [TO] MoEPostPermuteFwdOp: back to token order, routing weights applied, top-k
-    reduced, then the cast.
+    reduced, then the cast. Works for every layout: route_pos is the layout's inverse
+    index (the row of y holding route t*K + k). A negative position (a route a masked
+    slab had no room for) contributes nothing; the pages leave capacity overflow open and
+    this is the reading taken.
     """
     w = np.asarray(topk_weights, dtype=np.float64)
     T, K = w.shape
-    y = np.asarray(y, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64).reshape(-1, np.asarray(y).shape[-1])
     pos = np.asarray(route_pos, dtype=np.int64).reshape(T, K)
     out = np.zeros((T, y.shape[1]), dtype=np.float64)
     for k in range(K):
-        out += w[:, k:k + 1] * y[pos[:, k]]
+        live = pos[:, k] >= 0
+        out[live] += w[live, k:k + 1] * y[pos[live, k]]
     return round_to(float(scale) * out, out_dtype)
+
+
+# --------------------------------------------------------------------------------------
+# Padded and masked layouts.  [TO] MoEPermuteAlignFwdOp, MoEPrePermuteFwdOp,
+# MoEGroupedGemmFwdOp (layout table: contiguous with segment ends, contiguous with a
+# per-row expert id, masked [E, max_m, K] with valid counts), MoEPostPermuteFwdOp.
+def permute_align(topk_ids, num_experts: int, block_size: int):
+    """[TO] MoEPermuteAlignFwdOp: routes grouped by expert, each expert's range padded up
+    to a multiple of block_size.
+
+    Returns (sorted_token_ids, expert_ids, num_tokens_post_pad) with numel = T*K routes:
+    sorted_token_ids has numel + (E+1)(block_size-1) entries; expert e's range holds its
+    routes (ascending route index: the pages leave the order open) followed by numel up
+    to the padded length; every entry past num_tokens_post_pad is numel. expert_ids has
+    ceil(len / block_size) entries: the owner of each block of the ranges, then -1 (a
+    value outside [0, E)).
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    numel, E, bs = ids.size, num_experts, block_size
+    length = numel + (E + 1) * (bs - 1)
+    sorted_ids = np.full(length, numel, dtype=np.int64)
+    blocks = np.full(-(-length // bs), -1, dtype=np.int64)
+    start = 0
+    for e in range(E):
+        routes = np.nonzero(ids == e)[0]
+        padded = -(-routes.size // bs) * bs
+        sorted_ids[start:start + routes.size] = routes
+        blocks[start // bs:(start + padded) // bs] = e
+        start += padded
+    return sorted_ids, blocks, start
+
+
+def pre_permute(hidden, topk_ids, num_experts: int, layout: str, block_size: int = 1,
+                max_m: Optional[int] = None):
+    """[TO] MoEPrePermuteFwdOp: (expert_input, layout_metadata, inverse_indices).
+
+    layout "contiguous" (segment ends) or "per_row" (expert id per row): the rows of
+    permute_align(..., block_size) (block_size 1 = the tight layout), expert_input
+    [numel + E (block_size - 1), H] with pad rows and rows past the used length NaN
+    (unspecified); metadata = the E segment ends, or the expert of each row (-1 on pad
+    and unused rows). layout "masked": expert_input [E, max_m, H], metadata = rows placed
+    per expert, min(count, max_m); a route ranked max_m or later in its expert has no
+    room (inverse -1, the reading taken where the pages are silent). inverse_indices [T*K]:
+    the row of expert_input (flattened) holding route r = t*K + k, which reads hidden[t].
+    """
+    x = np.asarray(hidden, dtype=np.float64)
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    K = np.asarray(topk_ids).shape[-1]
+    numel, E, H = ids.size, num_experts, x.shape[1]
+    inverse = np.full(numel, -1, dtype=np.int64)
+    if layout == "masked":
+        out = np.full((E, max_m, H), np.nan)
+        counts = np.zeros(E, dtype=np.int64)
+        for e in range(E):
+            routes = np.nonzero(ids == e)[0][:max_m]
+            counts[e] = routes.size
+            out[e, :routes.size] = x[routes // K]
+            inverse[routes] = e * max_m + np.arange(routes.size)
+        return out, counts, inverse
+    sorted_ids, blocks, used = permute_align(ids, E, block_size)
+    cap = numel + E * (block_size - 1)
+    out = np.full((cap, H), np.nan)
+    live = np.nonzero(sorted_ids[:used] < numel)[0]
+    out[live] = x[sorted_ids[live] // K]
+    inverse[sorted_ids[live]] = live
+    if layout == "per_row":
+        meta = np.full(cap, -1, dtype=np.int64)
+        meta[live] = ids[sorted_ids[live]]
+        return out, meta, inverse
+    if layout == "contiguous":
+        ends = np.zeros(E, dtype=np.int64)
+        for e in range(E):
+            own = np.nonzero(blocks == e)[0]
+            ends[e] = (own[-1] + 1) * block_size if own.size else (ends[e - 1] if e else 0)
+        return out, ends, inverse
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def grouped_gemm_layout(a, b, layout: str, metadata, bias=None, act=None,
+                        out_dtype: str = "f32") -> np.ndarray:
+    """[TO] MoEGroupedGemmFwdOp over one of its layouts: out[rows of g] = a[rows of g]
+    b[g]^T (+ bias[g]), then the gated activation when act is given (F = N/2 columns).
+
+    contiguous: a [M, K], metadata = E segment ends (expert g owns rows end[g-1] ..
+    end[g]-1, end[-1] = 0). per_row: a [M, K], metadata [M] = expert of each row (rows
+    whose id is outside [0, E) belong to none). masked: a [E, max_m, K], metadata [E] =
+    valid rows, read as max_m when larger and 0 when negative. Rows owned by no expert,
+    and masked rows past the count, are NaN (unspecified).
+    """
+    b = [np.asarray(b[g], dtype=np.float64) for g in range(len(b))]
+    E, N = len(b), b[0].shape[0]
+    meta = np.asarray(metadata, dtype=np.int64)
+    a = np.asarray(a, dtype=np.float64)
+    masked = layout == "masked"
+    rows = a.reshape(-1, a.shape[-1])
+    owner = np.full(rows.shape[0], -1, dtype=np.int64)
+    if masked:
+        max_m = a.shape[1]
+        for g in range(E):
+            c = int(min(max(meta[g], 0), max_m))
+            owner[g * max_m:g * max_m + c] = g
+    elif layout == "contiguous":
+        lo = 0
+        for g in range(E):
+            owner[lo:meta[g]] = g
+            lo = meta[g]
+    elif layout == "per_row":
+        ok = (meta >= 0) & (meta < E)
+        owner[ok] = meta[ok]
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    h = np.full((rows.shape[0], N), np.nan)
+    for m in np.nonzero(owner >= 0)[0]:
+        g = owner[m]
+        h[m] = b[g] @ rows[m]
+        if bias is not None:
+            h[m] += np.asarray(bias[g], dtype=np.float64)
+    if act is not None:
+        params = _act_params(act)
+        gg, l = split_gate_up(h, params[0])
+        h = gated(gg, l, params)
+    out = round_to(h, out_dtype)
+    return out.reshape(*a.shape[:-1], out.shape[-1])
 
 
 def shared_expert_mlp(x, w_gate_up, w_down, dtype: str) -> np.ndarray:
@@ -565,6 +693,12 @@ PARITY_STATUS = {
     "gated": "pinned: gelu_and_mul brute force against torch's GELU; swiglu as above",
     "swiglu_op": "pinned: separate / stacked / interleaved forms agree, decimal closed "
                  "forms, bf16 store against torch's cast",
+    "permute_align": "pinned: the page's definition checked as invariants (per-expert "
+                     "route sets, padded lengths, numel fill, block owners, tail values)",
+    "pre_permute": "pinned: expert_input[inverse[r]] = hidden[r / K], the tight layout "
+                   "against permute(), masked counts and drops against brute-force ranks",
+    "grouped_gemm_layout": "pinned: per-row brute-force products; the three layouts of one "
+                           "routed problem agree route by route",
     "sqrt_softplus reading": "parity unpinned beyond the reading sqrt(softplus(z))",
     "gelu_and_mul reading": "the exact GELU is a reading (the pages name the activation "
                             "only); pinned as that reading",

@@ -608,4 +608,125 @@ def pin_swiglu_op_forms():
         assert np.array_equal(bf, torch.from_numpy(sep).to(torch.bfloat16).double().numpy())
 
 
+# ------------------------------------------------------------ padded / masked layouts
+def _routes_by_expert(ids, E):
+    return [[r for r in range(ids.size) if ids[r] == e] for e in range(E)]
+
+
+def pin_permute_align_definition():
+    """[TO] MoEPermuteAlignFwdOp's definition, checked entry by entry on random and
+    degenerate ids: each expert's range holds exactly its routes once, padded with numel
+    to a multiple of block_size; num_post_pad is the sum of the padded lengths; blocks
+    name their owner; everything past the used length is numel / outside [0, E)."""
+    r = _rng(31)
+    for T, K, E, bs in ((50, 3, 7, 16), (1, 1, 4, 64), (64, 8, 16, 1), (9, 2, 3, 5),
+                        (0, 2, 3, 4)):
+        ids = r.integers(0, E, size=(T, K)) if T else np.zeros((0, K), dtype=np.int64)
+        if T == 64:
+            ids[:] = 5          # one expert takes everything
+        flat = ids.reshape(-1)
+        numel = flat.size
+        st, blk, used = O.permute_align(ids, E, bs)
+        assert len(st) == numel + (E + 1) * (bs - 1)
+        assert len(blk) == -(-len(st) // bs)
+        want_used = sum(-(-len(rt) // bs) * bs for rt in _routes_by_expert(flat, E))
+        assert used == want_used and used % bs == 0
+        assert np.all(st[used:] == numel)
+        assert np.all((blk[used // bs:] < 0) | (blk[used // bs:] >= E))
+        start = 0
+        for e, rt in enumerate(_routes_by_expert(flat, E)):
+            n = -(-len(rt) // bs) * bs
+            seg = st[start:start + n]
+            assert sorted(seg[seg < numel].tolist()) == rt
+            assert np.all(seg[len(rt):] == numel)
+            assert np.all(blk[start // bs:(start + n) // bs] == e)
+            start += n
+
+
+def pin_pre_permute_layouts():
+    """Each layout puts hidden[r / K] at inverse[r]; the tight contiguous layout equals
+    permute() plus a gather; masked slabs keep the first max_m routes of an expert (in
+    route order) and drop the rest; per_row ids and segment ends describe the same rows."""
+    r = _rng(32)
+    T, K, E, H = 40, 3, 6, 5
+    x = r.standard_normal((T, H))
+    ids = r.integers(0, E, size=(T, K))
+    ids[:20, 0] = 2                       # expert 2 overflows a small slab
+    flat = ids.reshape(-1)
+    off, srt, pos = O.permute(ids, E)
+    for bs in (1, 4, 16):
+        outc, ends, invc = O.pre_permute(x, ids, E, "contiguous", bs)
+        outp, rowid, invp = O.pre_permute(x, ids, E, "per_row", bs)
+        assert np.array_equal(invc, invp) and np.array_equal(outc[invc], x[np.arange(T * K) // K])
+        for e in range(E):
+            lo = ends[e - 1] if e else 0
+            own = np.nonzero(rowid == e)[0]
+            assert np.all((own >= lo) & (own < ends[e])) and own.size == np.sum(flat == e)
+            assert (ends[e] - lo) % bs == 0
+        if bs == 1:
+            assert np.array_equal(invc, pos) and np.array_equal(ends, off[1:])
+    max_m = 9
+    outm, cnt, invm = O.pre_permute(x, ids, E, "masked", max_m=max_m)
+    for e in range(E):
+        rt = np.nonzero(flat == e)[0]
+        assert cnt[e] == min(rt.size, max_m)
+        assert np.array_equal(invm[rt[:max_m]], e * max_m + np.arange(cnt[e]))
+        assert np.all(invm[rt[max_m:]] == -1)
+    live = invm >= 0
+    assert np.array_equal(outm.reshape(-1, H)[invm[live]], x[np.nonzero(live)[0] // K])
+
+
+def pin_grouped_gemm_layouts():
+    """One routed problem laid out three ways: every route's product row agrees across
+    layouts and with a per-row brute-force dot product; uncovered rows are unspecified
+    (NaN); masked counts past max_m or negative are clamped."""
+    r = _rng(33)
+    T, K, E, H, N = 30, 2, 5, 7, 6
+    x = _f32(r.standard_normal((T, H)))
+    ids = r.integers(0, E, size=(T, K))
+    w = _f32(r.standard_normal((E, N, H)))
+    bias = _f32(r.standard_normal((E, N)))
+    flat = ids.reshape(-1)
+    want = np.array([w[flat[q]] @ x[q // K] + bias[flat[q]] for q in range(T * K)])
+    for lay, kw in (("contiguous", {"block_size": 4}), ("per_row", {"block_size": 8}),
+                    ("masked", {"max_m": 64})):
+        a, meta, inv = O.pre_permute(x, ids, E, lay, **kw)
+        out = O.grouped_gemm_layout(np.nan_to_num(a), w, lay, meta, bias, None, "f64")
+        flat_out = out.reshape(-1, N)
+        assert np.allclose(flat_out[inv], want, rtol=1e-12, atol=1e-12), lay
+        covered = np.zeros(flat_out.shape[0], bool)
+        covered[inv] = True
+        if lay != "contiguous":   # a contiguous segment also owns its pad rows
+            assert np.all(np.isnan(flat_out[~covered]))
+    # masked count clamping
+    a = _f32(r.standard_normal((3, 4, H)))
+    out = O.grouped_gemm_layout(a, w[:3], "masked", [9, -2, 2], None, None, "f64")
+    assert np.all(np.isfinite(out[0])) and np.all(np.isnan(out[1]))
+    assert np.all(np.isfinite(out[2, :2])) and np.all(np.isnan(out[2, 2:]))
+    # activation on a layout: gated product of the same rows
+    a, meta, inv = O.pre_permute(x, ids, E, "masked", max_m=64)
+    w2 = _f32(r.standard_normal((E, 2 * N, H)))
+    got = O.grouped_gemm_layout(a, w2, "masked", meta, None, "silu_and_mul", "f64")
+    for q in range(T * K):
+        h = w2[flat[q]] @ x[q // K]
+        g, u = h[:N], h[N:]
+        assert np.allclose(got.reshape(-1, N)[inv[q]], g / (1 + np.exp(-g)) * u, rtol=1e-12)
+
+
+def pin_combine_negative_positions():
+    """A route without a row (inverse -1) contributes nothing; the rest is the plain
+    weighted sum (brute force)."""
+    r = _rng(34)
+    T, K, H = 6, 3, 4
+    y = r.standard_normal((10, H))
+    w = r.standard_normal((T, K))
+    pos = r.integers(0, 10, size=(T, K))
+    pos[1, 2] = -1
+    pos[4, :] = -1
+    got = O.combine(y, w, pos.reshape(-1), 1.5, "f64")
+    for t in range(T):
+        want = sum(w[t, k] * y[pos[t, k]] for k in range(K) if pos[t, k] >= 0)
+        assert np.allclose(got[t], 1.5 * np.asarray(want, dtype=np.float64) if np.ndim(want) else np.zeros(H), atol=1e-14)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -180,7 +180,68 @@ def _swiglu_op_ignores_fusion(gate, up=None, alpha=1.0, beta=0.0, limit=0.0,
     return _orig_swiglu_op(gate, up, alpha, beta, limit, "stacked", out_dtype)
 
 
+_orig_permute_align = O.permute_align
+_orig_pre_permute = O.pre_permute
+_orig_gemm_layout = O.grouped_gemm_layout
+_orig_combine = O.combine
+
+
+def _align_extra_block(topk_ids, num_experts, block_size):
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    numel, E, bs = ids.size, num_experts, block_size
+    length = numel + (E + 1) * (bs - 1)
+    st = np.full(length, numel, dtype=np.int64)
+    blk = np.full(-(-length // bs), -1, dtype=np.int64)
+    start = 0
+    for e in range(E):
+        routes = np.nonzero(ids == e)[0]
+        padded = (routes.size // bs) * bs + (bs if routes.size else 0)  # one block too many
+        st[start:start + routes.size] = routes
+        blk[start // bs:(start + padded) // bs] = e
+        start += padded
+    return st, blk, start
+
+
+def _pre_permute_keeps_last(hidden, topk_ids, num_experts, layout, block_size=1, max_m=None):
+    if layout != "masked":
+        return _orig_pre_permute(hidden, topk_ids, num_experts, layout, block_size, max_m)
+    x = np.asarray(hidden, dtype=np.float64)
+    ids = np.asarray(topk_ids, dtype=np.int64).reshape(-1)
+    K = np.asarray(topk_ids).shape[-1]
+    E, H = num_experts, x.shape[1]
+    inv = np.full(ids.size, -1, dtype=np.int64)
+    out = np.full((E, max_m, H), np.nan)
+    cnt = np.zeros(E, dtype=np.int64)
+    for e in range(E):
+        rt = np.nonzero(ids == e)[0][-max_m:]
+        cnt[e] = rt.size
+        out[e, :rt.size] = x[rt // K]
+        inv[rt] = e * max_m + np.arange(rt.size)
+    return out, cnt, inv
+
+
+def _gemm_layout_per_row_shifted(a, b, layout, metadata, bias=None, act=None, out_dtype="f32"):
+    if layout == "per_row":
+        metadata = np.where(np.asarray(metadata) >= 0, (np.asarray(metadata) + 1) % len(b), -1)
+    return _orig_gemm_layout(a, b, layout, metadata, bias, act, out_dtype)
+
+
+def _combine_no_skip(y, topk_weights, route_pos, scale=1.0, out_dtype="f32"):
+    w = np.asarray(topk_weights, dtype=np.float64)
+    T, K = w.shape
+    yy = np.asarray(y, dtype=np.float64).reshape(-1, np.asarray(y).shape[-1])
+    pos = np.asarray(route_pos, dtype=np.int64).reshape(T, K)
+    out = np.zeros((T, yy.shape[1]))
+    for k in range(K):
+        out += w[:, k:k + 1] * yy[pos[:, k]]
+    return O.round_to(float(scale) * out, out_dtype)
+
+
 MUTANTS = {
+    "permute_align pads an exact multiple by one more block": ("permute_align", _align_extra_block),
+    "masked slab keeps the last routes": ("pre_permute", _pre_permute_keeps_last),
+    "per_row layout reads the next expert": ("grouped_gemm_layout", _gemm_layout_per_row_shifted),
+    "combine reads row -1 for a dropped route": ("combine", _combine_no_skip),
     "gelu by its tanh approximation": ("gelu", _gelu_tanh),
     "gelu_and_mul activates the up half": ("gated", _gated_act_on_up),
     "swiglu op reads interleaved input as stacked": ("swiglu_op", _swiglu_op_ignores_fusion),
