@@ -68,6 +68,16 @@ typedef enum { MOE_GU_STACKED = 0, MOE_GU_INTERLEAVED = 1 } moe_gu_layout;
 typedef enum { MOE_BACKEND_AUTO = 0, MOE_BACKEND_STAGED = 1, MOE_BACKEND_INDEXED = 2 }
     moe_backend;
 
+/* Expert row layouts of [TO] MoEGroupedGemmFwdOp's table:
+ *   CONTIGUOUS  rows [M, .] grouped by expert; metadata [E] = segment ends (expert g owns
+ *               rows end[g-1] .. end[g]-1, end[-1] = 0; segments may include padding)
+ *   PER_ROW     rows [M, .] grouped by expert; metadata [M] = expert id of each row (ids
+ *               outside [0, E) mark rows of no expert; each expert's rows form one run)
+ *   MASKED      slabs [E, max_m, .]; metadata [E] = valid rows of each expert, read as
+ *               max_m when larger and 0 when negative                               */
+typedef enum { MOE_LAYOUT_CONTIGUOUS = 0, MOE_LAYOUT_PER_ROW = 1, MOE_LAYOUT_MASKED = 2 }
+    moe_layout;
+
 /* Router options ([MR] MoERouter attributes; [TO] FusedTopKFwdOp __init__ and forward).
  *   top_k                 experts per token, 1 <= top_k <= min(E, 32)
  *   scoring               moe_scoring
@@ -232,16 +242,97 @@ int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, i
                      void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_grouped_gemm_layout - grouped GEMM over one of the layouts (moe_layout), with an
+ * optional gated activation.
+ * [TO] MoEGroupedGemmFwdOp (layout table; activation fused; bias added to the float32
+ * product before the activation; output in the operand dtype or float32).
+ *
+ * a        CONTIGUOUS / PER_ROW: [M, K] dt.  MASKED: [E, max_m, K] dt (M is ignored).
+ * b        [E, N, K] dt (with act: N = 2F gate/up rows in act->layout order).
+ * bias     [E, N] dt or NULL.
+ * layout_metadata  per layout (moe_layout), int32 on the device, not checked beyond
+ *          clamping every expert's rows into the rows that exist.
+ * act      NULL for a plain GEMM; else the gated activation (output width F = N/2).
+ * out      rows like a ([M, N or F], or [E, max_m, N or F]) in out_dt (dt or MOE_F32):
+ *          rows of an expert computed, rows of no expert (padding, masked rows past the
+ *          count) left unwritten. A CONTIGUOUS segment's padding rows are computed with
+ *          its expert's weights (their values are unspecified either way).
+ * workspace  PER_ROW: moe_grouped_gemm_layout_workspace_size(E) bytes (each expert's run,
+ *          found from the row ids); other layouts: may be NULL.
+ * Limits and errors as moe_grouped_gemm; INVALID_ARG for an unknown layout, max_m < 0,
+ * an odd N with act; WORKSPACE when PER_ROW lacks its workspace.
+ * ------------------------------------------------------------------------------- */
+size_t moe_grouped_gemm_layout_workspace_size(int64_t E);
+int moe_grouped_gemm_layout(const void* a, int64_t M, int64_t K, const void* b,
+                            const void* bias, int64_t E, int64_t N, int32_t layout,
+                            const int32_t* layout_metadata, int64_t max_m,
+                            const moe_act_cfg* act, int32_t dt, int32_t out_dt, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_permute_align - routes grouped by expert, each expert's range padded to a multiple
+ * of block_size.
+ * [TO] MoEPermuteAlignFwdOp. numel = T*K routes (route r = t*K + k), count[e] on expert e.
+ *
+ * sorted_token_ids  [numel + (E+1)(block_size-1)] int32 out: expert e's range (in expert
+ *          order, length count[e] rounded up to block_size) holds its routes in ascending
+ *          route index (the page leaves this order open), then numel; every entry past
+ *          num_tokens_post_pad is numel.
+ * expert_ids  [ceil(len(sorted_token_ids) / block_size)] int32 out: the owner of each
+ *          block of the ranges, -1 past them.
+ * num_tokens_post_pad  [1] int32 out: sum of the padded lengths.
+ * workspace  moe_layout_workspace_size(T, K, E, block_size) bytes.
+ * Limits: E <= 1024, block_size >= 1, numel + (E+1)(block_size-1) < 2^31.
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP, WORKSPACE.
+ * ------------------------------------------------------------------------------- */
+size_t moe_layout_workspace_size(int64_t T, int64_t K, int64_t E, int64_t block_size);
+int moe_permute_align(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                      int64_t block_size, int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_pad, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_pre_permute - token rows materialised in an expert layout.
+ * [TO] MoEPrePermuteFwdOp: (expert_input, layout_metadata, inverse_indices).
+ *
+ * hidden   [T, H] dt.   topk_ids [T, K] int32 in [0, E).
+ * CONTIGUOUS / PER_ROW (rows of moe_permute_align with block_size; 1 = unpadded):
+ *   expert_input  [T*K + E(block_size-1), H] dt: row m of the used length holds
+ *                 hidden[r / K] for the route r placed there; padding and rows past the
+ *                 used length are left unwritten.
+ *   layout_metadata  CONTIGUOUS: [E] segment ends; PER_ROW: [T*K + E(block_size-1)]
+ *                 expert id per row, -1 on padding and unused rows.
+ * MASKED (block_size ignored):
+ *   expert_input  [E, max_m, H] dt: slab row (e, j) holds the j-th route of expert e in
+ *                 route order, for j < min(count[e], max_m); other rows unwritten.
+ *   layout_metadata  [E] = min(count[e], max_m). A route ranked max_m or later in its
+ *                 expert has no room (the pages leave capacity overflow open).
+ * inverse_indices  [T*K] int32 out: the row of expert_input (flattened) holding route r,
+ *          or -1 for a route without room; moe_combine takes it as route_pos.
+ * workspace  moe_layout_workspace_size(T, K, E, block_size) bytes (1 for MASKED).
+ * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP, WORKSPACE.
+ * ------------------------------------------------------------------------------- */
+int moe_pre_permute(const void* hidden, int64_t T, int64_t H, int32_t dt,
+                    const int32_t* topk_ids, int64_t K, int64_t E, int32_t layout,
+                    int64_t block_size, int64_t max_m, void* expert_input,
+                    int32_t* layout_metadata, int32_t* inverse_indices, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_combine - back to token order, routing weights applied, top-k reduced, cast.
  * [TO] MoEPostPermuteFwdOp (weights applied exactly once), FusedMoEExpertsFwdOp.
  *
- * y               [R, H] in y_dt (MOE_F32 or the operand dtype), permuted rows.
- * topk_weights    [T, K] float32.   route_pos [T*K] int32 (from moe_permute).
+ * y               [y_rows, H] in y_dt (MOE_F32 or the operand dtype): expert outputs in
+ *                 any layout (a masked [E, max_m, H] slab is y_rows = E*max_m); every
+ *                 non-negative route_pos entry must be below y_rows.
+ * topk_weights    [T, K] float32.   route_pos [T*K] int32: the row of y holding each route
+ *                 (moe_permute's route_pos, or moe_pre_permute's inverse_indices); a
+ *                 negative entry contributes nothing.
  * out             [T, H] out_dt: scale * sum_k topk_weights[t,k] * y[route_pos[t*K+k]],
  *                 summed in float32 over k ascending, then rounded to out_dt.
  * Errors: INVALID_ARG, OVERLAP (out vs y, topk_weights, route_pos).
  * ------------------------------------------------------------------------------- */
-int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
+int moe_combine(const void* y, int32_t y_dt, int64_t y_rows, const float* topk_weights,
                 const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
                 void* out, int32_t out_dt, void* stream);
 

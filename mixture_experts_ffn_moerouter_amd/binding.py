@@ -34,7 +34,9 @@ SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute_worksp
            "moe_permute",
            "moe_grouped_gemm_swiglu", "moe_grouped_gemm", "moe_combine",
            "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward",
-           "moe_grouped_gemm_fp8_masked", "moe_swiglu")
+           "moe_grouped_gemm_fp8_masked", "moe_swiglu", "moe_grouped_gemm_layout_workspace_size",
+           "moe_grouped_gemm_layout", "moe_layout_workspace_size", "moe_permute_align",
+           "moe_pre_permute")
 
 
 class MoeRouteCfg(ctypes.Structure):
@@ -99,8 +101,22 @@ def lib():
         L.moe_grouped_gemm.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _I64, _I64, _P,
                                        _I32, _I32, _P, _P]
         L.moe_combine.restype = ctypes.c_int
-        L.moe_combine.argtypes = [_P, _I32, _P, _P, _I64, _I64, _I64, ctypes.c_float, _P,
-                                  _I32, _P]
+        L.moe_combine.argtypes = [_P, _I32, _I64, _P, _P, _I64, _I64, _I64, ctypes.c_float,
+                                  _P, _I32, _P]
+        L.moe_grouped_gemm_layout_workspace_size.restype = ctypes.c_size_t
+        L.moe_grouped_gemm_layout_workspace_size.argtypes = [_I64]
+        L.moe_grouped_gemm_layout.restype = ctypes.c_int
+        L.moe_grouped_gemm_layout.argtypes = [_P, _I64, _I64, _P, _P, _I64, _I64, _I32, _P,
+                                              _I64, ctypes.POINTER(MoeActCfg), _I32, _I32, _P,
+                                              _P, ctypes.c_size_t, _P]
+        L.moe_layout_workspace_size.restype = ctypes.c_size_t
+        L.moe_layout_workspace_size.argtypes = [_I64, _I64, _I64, _I64]
+        L.moe_permute_align.restype = ctypes.c_int
+        L.moe_permute_align.argtypes = [_P, _I64, _I64, _I64, _I64, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]
+        L.moe_pre_permute.restype = ctypes.c_int
+        L.moe_pre_permute.argtypes = [_P, _I64, _I64, _I32, _P, _I64, _I64, _I32, _I64, _I64,
+                                      _P, _P, _P, _P, ctypes.c_size_t, _P]
         L.moe_ffn_workspace_size.restype = ctypes.c_size_t
         L.moe_ffn_workspace_size.argtypes = [ctypes.POINTER(MoeFfnCfg)]
         L.moe_ffn_backend.restype = ctypes.c_int
@@ -252,13 +268,93 @@ def moe_grouped_gemm(a, b, expert_offsets, bias=None, out_dtype=None, a_rows=Non
 
 def moe_combine(y, topk_weights, route_pos, scale: float = 1.0, out_dtype=None, out=None,
                 stream=None):
+    """y: [rows, H] expert outputs, or a masked [E, max_m, H] slab; route_pos: the row of
+    each route (negative: no contribution)."""
     T, K = topk_weights.shape
-    H = y.shape[1]
+    H = y.shape[-1]
     out_dtype = y.dtype if out_dtype is None else out_dtype
     out = torch.empty((T, H), dtype=out_dtype, device=y.device) if out is None else out
     _check("moe_combine", lib().moe_combine(
-        _ptr(y), TORCH_DTYPES[y.dtype], _ptr(topk_weights), _ptr(route_pos), T, K, H,
-        float(scale), _ptr(out), TORCH_DTYPES[out_dtype], _stream(stream)))
+        _ptr(y), TORCH_DTYPES[y.dtype], y.numel() // max(H, 1), _ptr(topk_weights),
+        _ptr(route_pos), T, K, H, float(scale), _ptr(out), TORCH_DTYPES[out_dtype],
+        _stream(stream)))
+    return out
+
+
+LAYOUT_KINDS = {"contiguous": 0, "per_row": 1, "masked": 2}
+
+
+def moe_layout_workspace_size(T: int, K: int, E: int, block_size: int = 1) -> int:
+    return lib().moe_layout_workspace_size(T, K, E, block_size)
+
+
+def moe_permute_align(topk_ids, num_experts: int, block_size: int = 64, workspace=None,
+                      stream=None):
+    """[TO] MoEPermuteAlignFwdOp: (sorted_token_ids, expert_ids, num_tokens_post_pad)."""
+    T, K = topk_ids.shape
+    E, bs = num_experts, block_size
+    length = T * K + (E + 1) * (bs - 1)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(length, dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(-(-length // bs), dtype=torch.int32, device=dev)
+    num = torch.empty(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_layout_workspace_size(T, K, E, bs)),
+                                dtype=torch.uint8, device=dev)
+    _check("moe_permute_align", lib().moe_permute_align(
+        _ptr(topk_ids), T, K, E, bs, _ptr(sorted_ids), _ptr(expert_ids), _ptr(num),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return sorted_ids, expert_ids, num
+
+
+def moe_pre_permute(hidden, topk_ids, num_experts: int, layout: str = "contiguous",
+                    block_size: int = 1, max_m: int = 0, workspace=None, stream=None):
+    """[TO] MoEPrePermuteFwdOp: (expert_input, layout_metadata, inverse_indices)."""
+    T, H = hidden.shape
+    K = topk_ids.shape[1]
+    E = num_experts
+    dev = hidden.device
+    bs = 1 if layout == "masked" else block_size
+    if layout == "masked":
+        expert_input = torch.empty((E, max_m, H), dtype=hidden.dtype, device=dev)
+        meta = torch.empty(E, dtype=torch.int32, device=dev)
+    else:
+        cap = T * K + E * (bs - 1)
+        expert_input = torch.empty((cap, H), dtype=hidden.dtype, device=dev)
+        meta = torch.empty(cap if layout == "per_row" else E, dtype=torch.int32, device=dev)
+    inverse = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, moe_layout_workspace_size(T, K, E, bs)),
+                                dtype=torch.uint8, device=dev)
+    _check("moe_pre_permute", lib().moe_pre_permute(
+        _ptr(hidden), T, H, TORCH_DTYPES[hidden.dtype], _ptr(topk_ids), K, E,
+        LAYOUT_KINDS[layout], bs, max_m, _ptr(expert_input), _ptr(meta), _ptr(inverse),
+        _ptr(workspace), workspace.numel(), _stream(stream)))
+    return expert_input, meta, inverse
+
+
+def moe_grouped_gemm_layout(a, b, layout: str, layout_metadata, bias=None, act=None,
+                            out_dtype=None, out=None, workspace=None, stream=None):
+    """[TO] MoEGroupedGemmFwdOp over a layout: a [M, K] (contiguous, per_row) or
+    [E, max_m, K] (masked); act None (plain) or a gated activation."""
+    E, N, K = b.shape
+    masked = layout == "masked"
+    M = 0 if masked else a.shape[0]
+    max_m = a.shape[1] if masked else 0
+    Nout = N // 2 if act is not None else N
+    out_dtype = a.dtype if out_dtype is None else out_dtype
+    if out is None:
+        shape = (E, max_m, Nout) if masked else (M, Nout)
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    if workspace is None and layout == "per_row":
+        workspace = torch.empty(lib().moe_grouped_gemm_layout_workspace_size(E),
+                                dtype=torch.uint8, device=a.device)
+    ac = act_cfg(act) if act is not None else None
+    _check("moe_grouped_gemm_layout", lib().moe_grouped_gemm_layout(
+        _ptr(a), M, K, _ptr(b), _ptr(bias), E, N, LAYOUT_KINDS[layout], _ptr(layout_metadata),
+        max_m, ctypes.byref(ac) if ac is not None else None, TORCH_DTYPES[a.dtype],
+        TORCH_DTYPES[out_dtype], _ptr(out), _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(stream)))
     return out
 
 

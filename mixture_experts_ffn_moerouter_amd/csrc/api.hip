@@ -122,6 +122,32 @@ int check_ffn_cfg(const moe_ffn_cfg* c) {
   return MOE_OK;
 }
 
+// Workspace of moe_permute_align / moe_pre_permute: the tight permute, then the padded
+// offsets, sorted_token_ids and block owners.
+struct LayoutWs {
+  size_t off, sorted, pos, blk_cnt, padded, sorted_ids, expert_blk, total;
+};
+
+LayoutWs layout_ws(int64_t R, int64_t E, int64_t bs) {
+  LayoutWs w;
+  const size_t len = (size_t)(R + (E + 1) * (bs - 1)), nblk = (len + bs - 1) / bs;
+  size_t o = 0;
+  w.off = o; o += align256((size_t)(E + 1) * 4);
+  w.sorted = o; o += align256((size_t)R * 4);
+  w.pos = o; o += align256((size_t)R * 4);
+  w.blk_cnt = o; o += align256(permute_workspace_bytes((int)R, (int)E));
+  w.padded = o; o += align256((size_t)(E + 1) * 4);
+  w.sorted_ids = o; o += align256(len * 4);
+  w.expert_blk = o; o += align256(nblk * 4);
+  w.total = o;
+  return w;
+}
+
+bool layout_sizes_ok(int64_t T, int64_t K, int64_t E, int64_t bs) {
+  return T >= 0 && K >= 1 && E >= 1 && bs >= 1 && bs <= (1 << 20) &&
+         T * K + (E + 1) * (bs - 1) < ((int64_t)1 << 31);
+}
+
 int backend_for(const moe_ffn_cfg& c, bool has_bias) {
   const bool indexed_shape = c.dtype != MOE_F32 && is_silu_and_mul(c.act) && !has_bias &&
                              c.H % 128 == 0 && c.F % 256 == 0;
@@ -223,11 +249,14 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
                                       permuted, s));
 }
 
+// seg_mode / max_m describe `offsets` (kSegOffsets: [E+1]; kSegEnds: [E]; kSegMasked:
+// counts [E]; kSegRuns: [2E] pairs written by the per-row pre-pass).
 static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_rows_div,
                                int64_t M, int64_t Kd, const void* b, const void* bias,
                                int64_t E, int64_t Nw, bool act_on, const moe_act_cfg* act,
                                const int32_t* offsets, int32_t dt, int32_t out_dt, void* out,
-                               void* stream) {
+                               void* stream, int seg_mode = kSegOffsets, int64_t max_m = 0,
+                               void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (!b || !offsets || M < 0 || Kd < 1 || E < 1 || Nw < 1) return MOE_ERR_INVALID_ARG;
   if (M > 0 && (!a || !out)) return MOE_ERR_INVALID_ARG;
   if (a_rows && a_rows_div < 1) return MOE_ERR_INVALID_ARG;
@@ -243,12 +272,22 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   if (dt == MOE_F32 && Kd > 12288) return MOE_ERR_UNSUPPORTED;  // A row staged in LDS
   const int64_t Nout = act_on ? Nw / 2 : Nw;
   const size_t s = dt_size(dt);
+  const size_t meta_bytes = seg_mode == kSegOffsets ? (size_t)(E + 1) * 4
+                            : seg_mode == kSegRuns ? (size_t)M * 4 : (size_t)E * 4;
+  const size_t ws_need = seg_mode == kSegRuns ? (size_t)E * 8 : 0;
+  if (ws_need && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
   Range ins[] = {{b, (size_t)E * Nw * Kd * s}, {bias, bias ? (size_t)E * Nw * s : 0},
-                 {offsets, (size_t)(E + 1) * 4}, {a_rows, a_rows ? (size_t)M * 4 : 0},
+                 {offsets, meta_bytes}, {a_rows, a_rows ? (size_t)M * 4 : 0},
                  {a, a_rows ? 1 : (size_t)M * Kd * s}};
-  Range outs[] = {{out, (size_t)M * Nout * dt_size(out_dt)}};
-  if (any_overlap(outs, 1, ins, 5)) return MOE_ERR_OVERLAP;
+  Range outs[] = {{out, (size_t)M * Nout * dt_size(out_dt)}, {workspace, ws_need}};
+  if (any_overlap(outs, 2, ins, 5)) return MOE_ERR_OVERLAP;
   if (M == 0) return MOE_OK;
+  if (seg_mode == kSegRuns) {  // per-row ids -> [start, end) of each expert's run
+    int st = status_of(launch_row_runs(offsets, (int)M, (int)E, (int32_t*)workspace,
+                                       (hipStream_t)stream));
+    if (st) return st;
+    offsets = (const int32_t*)workspace;
+  }
   GemmArgs g;
   g.a = a;
   g.a_rows = a_rows;
@@ -258,6 +297,8 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   g.b = b;
   g.bias = bias;
   g.offsets = offsets;
+  g.seg_mode = seg_mode;
+  g.max_m = (int)max_m;
   g.E = (int)E;
   g.Nw = (int)Nw;
   g.act = act_on;
@@ -289,6 +330,118 @@ int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, i
                      void* stream) {
   return grouped_gemm_common(a, a_rows, a_rows_div, M, K, b, bias, E, N, false, nullptr,
                              expert_offsets, dt, out_dt, out, stream);
+}
+
+size_t moe_grouped_gemm_layout_workspace_size(int64_t E) {
+  return E >= 1 && E <= kMaxGemmE ? align256((size_t)E * 8) : 0;
+}
+
+int moe_grouped_gemm_layout(const void* a, int64_t M, int64_t K, const void* b,
+                            const void* bias, int64_t E, int64_t N, int32_t layout,
+                            const int32_t* layout_metadata, int64_t max_m,
+                            const moe_act_cfg* act, int32_t dt, int32_t out_dt, void* out,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  int mode;
+  int64_t rows = M;
+  if (layout == MOE_LAYOUT_CONTIGUOUS) {
+    mode = kSegEnds;
+  } else if (layout == MOE_LAYOUT_PER_ROW) {
+    mode = kSegRuns;
+  } else if (layout == MOE_LAYOUT_MASKED) {
+    if (max_m < 0 || E < 1) return MOE_ERR_INVALID_ARG;
+    if (E * max_m >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+    mode = kSegMasked;
+    rows = E * max_m;
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  if (act && N % 2) return MOE_ERR_INVALID_ARG;
+  return grouped_gemm_common(a, nullptr, 1, rows, K, b, bias, E, N, act != nullptr, act,
+                             layout_metadata, dt, out_dt, out, stream, mode, max_m, workspace,
+                             workspace_bytes);
+}
+
+size_t moe_layout_workspace_size(int64_t T, int64_t K, int64_t E, int64_t block_size) {
+  if (!layout_sizes_ok(T, K, E, block_size) || E > kMaxGemmE) return 0;
+  return layout_ws(T * K, E, block_size).total;
+}
+
+int moe_permute_align(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
+                      int64_t block_size, int32_t* sorted_token_ids, int32_t* expert_ids,
+                      int32_t* num_tokens_post_pad, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!layout_sizes_ok(T, K, E, block_size)) return MOE_ERR_INVALID_ARG;
+  if (!sorted_token_ids || !expert_ids || !num_tokens_post_pad || (T > 0 && !topk_ids))
+    return MOE_ERR_INVALID_ARG;
+  if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
+  const int64_t R = T * K, bs = block_size;
+  const size_t len = (size_t)align_len((int)R, (int)E, (int)bs), nblk = (len + bs - 1) / bs;
+  const LayoutWs w = layout_ws(R, E, bs);
+  if (!workspace || workspace_bytes < w.total) return MOE_ERR_WORKSPACE;
+  Range ins[] = {{topk_ids, (size_t)R * 4}};
+  Range outs[] = {{sorted_token_ids, len * 4}, {expert_ids, nblk * 4},
+                  {num_tokens_post_pad, 4}, {workspace, w.total}};
+  if (any_overlap(outs, 4, ins, 1)) return MOE_ERR_OVERLAP;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int st = status_of(launch_permute(topk_ids, (int)R, (int)E, (int32_t*)(ws + w.off),
+                                    (int32_t*)(ws + w.sorted), (int32_t*)(ws + w.pos), nullptr,
+                                    (int32_t*)(ws + w.blk_cnt), s));
+  if (st) return st;
+  return status_of(launch_align((int32_t*)(ws + w.off), (int32_t*)(ws + w.sorted), (int)R,
+                                (int)E, (int)bs, (int32_t*)(ws + w.padded), sorted_token_ids,
+                                expert_ids, num_tokens_post_pad, nullptr, s));
+}
+
+int moe_pre_permute(const void* hidden, int64_t T, int64_t H, int32_t dt,
+                    const int32_t* topk_ids, int64_t K, int64_t E, int32_t layout,
+                    int64_t block_size, int64_t max_m, void* expert_input,
+                    int32_t* layout_metadata, int32_t* inverse_indices, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const bool masked = layout == MOE_LAYOUT_MASKED;
+  if (layout < MOE_LAYOUT_CONTIGUOUS || layout > MOE_LAYOUT_MASKED) return MOE_ERR_INVALID_ARG;
+  const int64_t bs = masked ? 1 : block_size;
+  if (!layout_sizes_ok(T, K, E, bs) || H < 1 || (masked && max_m < 0)) return MOE_ERR_INVALID_ARG;
+  if (!any_dt_ok(dt)) return MOE_ERR_UNSUPPORTED;
+  if (E > kMaxGemmE) return MOE_ERR_UNSUPPORTED;
+  const int64_t R = T * K;
+  const int64_t cap = masked ? E * max_m : R + E * (bs - 1);
+  if (cap >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!layout_metadata || (R > 0 && (!hidden || !topk_ids || !inverse_indices)) ||
+      (cap > 0 && !expert_input))
+    return MOE_ERR_INVALID_ARG;
+  const size_t row = (size_t)H * dt_size(dt);
+  const size_t meta_n = layout == MOE_LAYOUT_PER_ROW ? (size_t)cap : (size_t)E;
+  const LayoutWs w = layout_ws(R, E, bs);
+  if (!workspace || workspace_bytes < w.total) return MOE_ERR_WORKSPACE;
+  Range ins[] = {{hidden, (size_t)T * row}, {topk_ids, (size_t)R * 4}};
+  Range outs[] = {{expert_input, (size_t)cap * row}, {layout_metadata, meta_n * 4},
+                  {inverse_indices, (size_t)R * 4}, {workspace, w.total}};
+  if (any_overlap(outs, 4, ins, 2)) return MOE_ERR_OVERLAP;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int32_t* off = (int32_t*)(ws + w.off);
+  int32_t* sorted = (int32_t*)(ws + w.sorted);
+  int st = status_of(launch_permute(topk_ids, (int)R, (int)E, off, sorted,
+                                    (int32_t*)(ws + w.pos), nullptr,
+                                    (int32_t*)(ws + w.blk_cnt), s));
+  if (st) return st;
+  if (masked)
+    return status_of(launch_masked_rows(hidden, (int64_t)row, (int)K, (int)R, off, sorted,
+                                        (int)E, (int)max_m, expert_input, layout_metadata,
+                                        inverse_indices, s));
+  int32_t* padded = (int32_t*)(ws + w.padded);
+  int32_t* sorted_ids = (int32_t*)(ws + w.sorted_ids);
+  int32_t* expert_blk = (int32_t*)(ws + w.expert_blk);
+  st = status_of(launch_align(off, sorted, (int)R, (int)E, (int)bs, padded, sorted_ids,
+                              expert_blk, nullptr,
+                              layout == MOE_LAYOUT_CONTIGUOUS ? layout_metadata : nullptr, s));
+  if (st) return st;
+  return status_of(launch_contiguous_rows(hidden, (int64_t)row, (int)K, sorted_ids, expert_blk,
+                                          padded, (int)E, (int)bs, (int)R, (int)cap,
+                                          expert_input, inverse_indices,
+                                          layout == MOE_LAYOUT_PER_ROW ? layout_metadata : nullptr,
+                                          s));
 }
 
 int moe_grouped_gemm_fp8_masked(const void* a, const float* a_scale, const void* b,
@@ -347,15 +500,16 @@ int moe_swiglu(const void* gate, const void* up, int64_t rows, int64_t F, int32_
   return status_of(launch_swiglu(a, (hipStream_t)stream));
 }
 
-int moe_combine(const void* y, int32_t y_dt, const float* topk_weights,
+int moe_combine(const void* y, int32_t y_dt, int64_t y_rows, const float* topk_weights,
                 const int32_t* route_pos, int64_t T, int64_t K, int64_t H, float scale,
                 void* out, int32_t out_dt, void* stream) {
-  if (T < 0 || K < 1 || H < 1) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || K < 1 || H < 1 || y_rows < 0) return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!y || !topk_weights || !route_pos || !out)) return MOE_ERR_INVALID_ARG;
   if (!operand_dt_ok(y_dt) || !any_dt_ok(out_dt)) return MOE_ERR_UNSUPPORTED;
   if (T * K >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
   const size_t R = (size_t)(T * K);
-  Range ins[] = {{y, R * H * dt_size(y_dt)}, {topk_weights, R * 4}, {route_pos, R * 4}};
+  Range ins[] = {{y, (size_t)y_rows * H * dt_size(y_dt)}, {topk_weights, R * 4},
+                 {route_pos, R * 4}};
   Range outs[] = {{out, (size_t)T * H * dt_size(out_dt)}};
   if (any_overlap(outs, 1, ins, 3)) return MOE_ERR_OVERLAP;
   if (T == 0) return MOE_OK;
@@ -483,6 +637,8 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
     g.b = w_gate_up;
     g.bias = b_gate_up;
     g.offsets = offsets;
+    g.seg_mode = kSegOffsets;
+    g.max_m = 0;
     g.E = (int)E;
     g.Nw = (int)(2 * F);
     g.act = 1;
@@ -525,6 +681,8 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
     g.b = shared_w_gate_up;
     g.bias = nullptr;
     g.offsets = nullptr;
+    g.seg_mode = kSegOffsets;
+    g.max_m = 0;
     g.E = 1;
     g.Nw = (int)(2 * Fs);
     g.act = 1;

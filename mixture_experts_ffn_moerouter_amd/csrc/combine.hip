@@ -2,7 +2,9 @@
 //
 // [TO] TileOPs "MoE Operators", MoEPostPermuteFwdOp (token order restored, routing
 //      weights applied once, top-k reduced, then cast) and FusedMoEExpertsFwdOp
-//      (output[t] = scale * sum_k w[t,k] * expert output of route (t, k)).
+//      (output[t] = scale * sum_k w[t,k] * expert output of route (t, k)). route_pos is
+//      any layout's inverse index; a negative entry (a route a masked slab had no room
+//      for) contributes nothing.
 //
 // One workgroup per token; each thread owns 8 consecutive hidden elements (16-byte
 // loads of 16-bit rows), sums its K rows in float32 in k order and writes once.
@@ -43,6 +45,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int k = 0; k < K; ++k) {
+        if (pt[k] < 0) continue;  // a route without a row contributes nothing
         float v[8];
         load8<YDT>((const char*)y + ((int64_t)pt[k] * H + h) * ysz, v);
         const float wk = wt[k];
@@ -67,6 +70,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     for (int h = threadIdx.x; h < H; h += blockDim.x) {
       float acc = 0.f;
       for (int k = 0; k < K; ++k) {
+        if (pt[k] < 0) continue;
         const float v = load_dt(y, YDT, (int64_t)pt[k] * H + h);
         acc = fmaf(wt[k], v, acc);
       }

@@ -87,19 +87,21 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
   constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * WN;
   constexpr int NLD = (BMX * BK / 8) / NT, NLDB = (BNW * BK / 8) / NT;
   constexpr int kStageElems = stage_elems<RB, CB, BK, NT, WM>();
-  static_assert(lds_bytes<RB, CB, BK, NT, WM, NBUF>() >= 2 * (kMaxE + 1) * sizeof(int),
+  static_assert(lds_bytes<RB, CB, BK, NT, WM, NBUF>() >= 3 * (kMaxE + 1) * sizeof(int),
                 "tile map alias");
   static_assert(NBUF == 2 || PA == 1, "one LDS buffer goes with A one step ahead");
   static_assert(NBUF == 2 || MID >= BK / 16, "one LDS buffer: the store follows the last MFMA");
   static_assert(CB == 2 || CB == 4, "weight blocks per wave");
   __shared__ int s_tmp[NT / 64];
   extern __shared__ __align__(16) uint16_t smem[];  // [2][BMX + BNW][LDK]
-  int* s_off = (int*)smem;  // the tile map lives in the stage buffers until the K loop
-  int* s_pre = s_off + kMaxE + 1;
+  int* s_start = (int*)smem;  // the tile map lives in the stage buffers until the K loop
+  int* s_len = s_start + kMaxE + 1;
+  int* s_pre = s_len + kMaxE + 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = g.E;
-  build_tile_map<NT>(g.offsets, E, g.M, BMX, s_off, s_pre, s_tmp);
+  build_tile_map_segments<NT>(g.seg_mode, g.offsets, E, g.M, g.max_m, BMX, s_start, s_len,
+                              s_pre, s_tmp);
 
   const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
   const int n_valid = s_pre[E] * n_tiles_n;
@@ -114,9 +116,9 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
   const int t_e = s_pre[e + 1] - s_pre[e];
   const int local = L - s_pre[e] * n_tiles_n;
   const int nt = local / t_e, mt = local % t_e;
-  const int rpt = rows_per_tile(s_off[e + 1] - s_off[e], BMX);
-  const int m0 = s_off[e] + mt * rpt;
-  const int m1 = min(m0 + rpt, s_off[e + 1]);
+  const int rpt = rows_per_tile(s_len[e], BMX);
+  const int m0 = s_start[e] + mt * rpt;
+  const int m1 = min(m0 + rpt, s_start[e] + s_len[e]);
   const int rows = m1 - m0;
   const int nb = (rows + 31) / 32;  // live 32-row blocks
   const int Kd = g.Kd;
@@ -365,20 +367,42 @@ __global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
 // float32 operands: one workgroup per output row; the A row is staged in LDS and each
 // thread forms the dot products of its output column(s). Plain FMA arithmetic; meant
 // for small float32 problems.
+// Expert owning row m under the segment metadata of g (see GemmArgs), or -1.
+__device__ int row_owner(const GemmArgs& g, int m) {
+  const int32_t* meta = g.offsets;
+  if (g.seg_mode == kSegMasked) {
+    const int e = m / g.max_m;
+    return m % g.max_m < min(max(meta[e], 0), g.max_m) ? e : -1;
+  }
+  if (g.seg_mode == kSegRuns) {
+    for (int e = 0; e < g.E; ++e)
+      if (m >= meta[2 * e] && m < meta[2 * e + 1]) return e;
+    return -1;
+  }
+  if (g.seg_mode == kSegEnds) {  // smallest e with ends[e] > m
+    if (m >= meta[g.E - 1]) return -1;
+    int lo = 0, hi = g.E - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (meta[mid] > m) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+  }
+  if (!meta) return 0;  // one expert owning every row
+  if (m < meta[0] || m >= meta[g.E]) return -1;
+  int lo = 0, hi = g.E - 1;  // largest e with off[e] <= m
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (meta[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   extern __shared__ float srow[];
   const int m = blockIdx.x;
-  const int32_t* off = g.offsets;  // NULL: one expert owning every row
-  int e = 0;
-  if (off) {
-    if (m < off[0] || m >= off[g.E]) return;
-    int lo = 0, hi = g.E - 1;  // largest e with off[e] <= m
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= m) lo = mid; else hi = mid - 1;
-    }
-    e = lo;
-  }
+  const int e = row_owner(g, m);
+  if (e < 0) return;
   const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
   const float* a = (const float*)g.a + (int64_t)src * g.Kd;
   for (int k = threadIdx.x; k < g.Kd; k += blockDim.x) srow[k] = a[k];

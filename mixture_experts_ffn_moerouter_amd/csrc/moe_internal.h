@@ -97,6 +97,29 @@ hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets,
 hipError_t launch_gather_rows(const void* src, const int32_t* rows, int div, int M,
                               int64_t row_bytes, void* dst, hipStream_t s);
 
+// Padded and masked layouts (layout.hip). align_len = entries of sorted_token_ids.
+__host__ __device__ inline int align_len(int R, int E, int bs) { return R + (E + 1) * (bs - 1); }
+hipError_t launch_align(const int32_t* off, const int32_t* sorted_route, int R, int E, int bs,
+                        int32_t* padded_off, int32_t* sorted_ids, int32_t* expert_blk,
+                        int32_t* num_post_pad, int32_t* seg_ends, hipStream_t s);
+hipError_t launch_contiguous_rows(const void* hidden, int64_t row_bytes, int K,
+                                  const int32_t* sorted_ids, const int32_t* expert_blk,
+                                  const int32_t* padded_off, int E, int bs, int R, int cap,
+                                  void* out, int32_t* inverse, int32_t* row_ids,
+                                  hipStream_t s);
+hipError_t launch_masked_rows(const void* hidden, int64_t row_bytes, int K, int R,
+                              const int32_t* off, const int32_t* sorted_route, int E,
+                              int max_m, void* out, int32_t* counts, int32_t* inverse,
+                              hipStream_t s);
+hipError_t launch_row_runs(const int32_t* ids, int M, int E, int32_t* pairs, hipStream_t s);
+
+// Row segments of the experts in a grouped GEMM (see build_tile_map_segments):
+//   kSegOffsets  offsets[E+1] (tight layout; null = one expert owning rows 0 .. M-1)
+//   kSegEnds     segment ends[E] (contiguous layout, possibly padded)
+//   kSegMasked   counts[E], expert e owns rows e*max_m .. e*max_m + clamp(count) - 1
+//   kSegRuns     pairs[2E] of [start, end) (the per-row layout, after launch_row_runs)
+enum { kSegOffsets = 0, kSegEnds = 1, kSegMasked = 2, kSegRuns = 3 };
+
 struct GemmArgs {
   const void* a;
   const int32_t* a_rows;
@@ -104,7 +127,9 @@ struct GemmArgs {
   int M, Kd;          // logical rows, contraction length
   const void* b;      // [E, Nw, Kd]
   const void* bias;   // [E, Nw] or null
-  const int32_t* offsets;
+  const int32_t* offsets;  // segment metadata, per seg_mode
+  int seg_mode;
+  int max_m;          // kSegMasked
   int E, Nw;          // weight rows per expert
   int act;            // 0 none, 1 gated activation
   int act_kind;       // 0 swiglu family (alpha, beta, limit), 1 gelu_and_mul

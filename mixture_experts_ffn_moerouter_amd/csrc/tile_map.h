@@ -47,14 +47,35 @@ __device__ void scan_tiles(int E, int bm, RowsOf rows_of, int* s_pre, int* s_tmp
   __syncthreads();
 }
 
-// Tight layout: copies the offsets into s_off (offsets == NULL means one expert that owns
-// rows 0 .. M-1) and builds s_pre.
+// Any layout: s_start[e] / s_len[e] = expert e's rows [start, start + len) inside [0, M),
+// from the metadata per mode (kSegOffsets, kSegEnds, kSegMasked, kSegRuns; see GemmArgs),
+// clamped to the rows that exist; and s_pre.
 template <int NT>
-__device__ void build_tile_map(const int32_t* offsets, int E, int M, int bm, int* s_off,
-                               int* s_pre, int* s_tmp) {
-  for (int i = threadIdx.x; i <= E; i += NT) s_off[i] = offsets ? offsets[i] : (i == 0 ? 0 : M);
+__device__ void build_tile_map_segments(int mode, const int32_t* meta, int E, int M, int max_m,
+                                        int bm, int* s_start, int* s_len, int* s_pre,
+                                        int* s_tmp) {
+  for (int e = threadIdx.x; e < E; e += NT) {
+    int lo, hi;
+    if (mode == kSegOffsets) {
+      lo = meta ? meta[e] : (e == 0 ? 0 : M);
+      hi = meta ? meta[e + 1] : M;
+    } else if (mode == kSegEnds) {
+      lo = e ? meta[e - 1] : 0;
+      hi = meta[e];
+    } else if (mode == kSegMasked) {
+      lo = e * max_m;
+      hi = lo + min(max(meta[e], 0), max_m);
+    } else {
+      lo = meta[2 * e];
+      hi = meta[2 * e + 1];
+    }
+    lo = min(max(lo, 0), M);
+    hi = min(max(hi, lo), M);
+    s_start[e] = lo;
+    s_len[e] = hi - lo;
+  }
   __syncthreads();
-  scan_tiles<NT>(E, bm, [&](int e) { return s_off[e + 1] - s_off[e]; }, s_pre, s_tmp);
+  scan_tiles<NT>(E, bm, [&](int e) { return s_len[e]; }, s_pre, s_tmp);
 }
 
 // Masked layout: s_cnt[e] = counts[e] clamped to [0, max_m], and s_pre.

@@ -38,6 +38,9 @@ class LazyExperts:
     def __getitem__(self, e):
         return np64(self.t[int(e)])
 
+    def __len__(self):
+        return self.t.shape[0]
+
 
 def assert_close(got, ref, dtype: str, what: str = ""):
     got = np.asarray(got, np.float64)

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 18, names
     assert set(names) == set(B.SYMBOLS)
     L = B.lib()
     for n in names:
@@ -135,7 +135,7 @@ def test_gemm_combine_permute_argument_errors():
     assert st == B.MOE_ERR_UNSUPPORTED
     st = L.moe_grouped_gemm(None, None, 1, 16, 64, FAKE, None, 2, 32, FAKE, 1, 1, FAKE, None)
     assert st == B.MOE_ERR_INVALID_ARG
-    st = L.moe_combine(FAKE, 1, FAKE + (1 << 20), FAKE + (1 << 21), 4, 2, 64, 1.0, FAKE + 32,
+    st = L.moe_combine(FAKE, 1, 8, FAKE + (1 << 20), FAKE + (1 << 21), 4, 2, 64, 1.0, FAKE + 32,
                        1, None)
     assert st == B.MOE_ERR_OVERLAP
     WS = FAKE + (1 << 30)
@@ -232,3 +232,36 @@ def test_swiglu_argument_errors():
     assert f(out=U + 100) == B.MOE_ERR_OVERLAP               # out over up
     assert f(u=None, out=G + 16 * 64 * 2 + 2) == B.MOE_ERR_OVERLAP  # inside fused [16, 128]
     assert f(rows=0, g=None, u=None, out=None) == B.MOE_OK
+
+
+def test_layout_argument_errors():
+    L = B.lib()
+    IDS, SID, EID, NUM, WS = (FAKE + i * (1 << 32) for i in range(5))
+    need = B.moe_layout_workspace_size(10, 2, 8, 16)
+    assert need > 0 and B.moe_layout_workspace_size(10, 2, 2000, 16) == 0
+    al = lambda T=10, K=2, E=8, bs=16, ids=IDS, sid=SID, eid=EID, num=NUM, ws=WS, n=need: \
+        L.moe_permute_align(ids, T, K, E, bs, sid, eid, num, ws, n, None)
+    assert al(bs=0) == B.MOE_ERR_INVALID_ARG
+    assert al(sid=None) == B.MOE_ERR_INVALID_ARG
+    assert al(E=2000) == B.MOE_ERR_UNSUPPORTED
+    assert al(n=need - 1) == B.MOE_ERR_WORKSPACE
+    assert al(sid=IDS + 16) == B.MOE_ERR_OVERLAP          # sorted ids over topk_ids
+    assert al(num=WS + 8) == B.MOE_ERR_OVERLAP            # count inside the workspace
+    HID, OUT, META, INV = (FAKE + i * (1 << 34) for i in range(4))
+    pp = lambda layout=0, bs=4, max_m=8, dt=1, out=OUT, meta=META, n=need: L.moe_pre_permute(
+        HID, 10, 64, dt, IDS, 2, 8, layout, bs, max_m, out, meta, INV, WS, n, None)
+    assert pp(layout=3) == B.MOE_ERR_INVALID_ARG
+    assert pp(layout=2, max_m=-1) == B.MOE_ERR_INVALID_ARG
+    assert pp(dt=5) == B.MOE_ERR_UNSUPPORTED
+    assert pp(meta=None) == B.MOE_ERR_INVALID_ARG
+    assert pp(out=HID + 64) == B.MOE_ERR_OVERLAP
+    assert pp(n=0) == B.MOE_ERR_WORKSPACE
+    act = B.act_cfg("silu_and_mul")
+    W, A, O = FAKE, FAKE + (1 << 34), FAKE + (1 << 35)
+    gl = lambda layout=1, N=64, ws=None, wsn=0, act_=None, max_m=0: L.moe_grouped_gemm_layout(
+        A, 32, 64, W, None, 4, N, layout, FAKE + (1 << 36), max_m, act_, 1, 1, O, ws, wsn, None)
+    assert gl() == B.MOE_ERR_WORKSPACE                     # per_row needs its run table
+    assert gl(layout=7) == B.MOE_ERR_INVALID_ARG
+    assert gl(layout=2, max_m=-1) == B.MOE_ERR_INVALID_ARG
+    assert gl(layout=0, N=63, act_=ctypes.byref(act)) == B.MOE_ERR_INVALID_ARG
+    assert B.lib().moe_grouped_gemm_layout_workspace_size(4) >= 32

@@ -1,0 +1,189 @@
+"""Padded and masked layouts (moe_permute_align, moe_pre_permute, moe_grouped_gemm_layout,
+moe_combine with inverse indices) against the oracle.
+
+Integer outputs and copied rows are compared bit for bit; GEMM outputs to the dtype's
+bound. Rows a layout leaves unspecified are checked to be untouched (a sentinel)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_ffn_moerouter_amd import binding as B
+from mixture_experts_ffn_moerouter_amd import inputs as I
+from moe_testlib import LazyExperts, assert_close, np64, say
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+SENTINEL = -12288.0  # exactly representable in every dtype used here
+
+
+def _ids(T, K, E, seed, hot=None):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    ids = torch.randint(0, E, (T, K), device="cuda", generator=g, dtype=torch.int32)
+    if hot is not None and T:
+        ids[: T // 2, 0] = hot  # one expert takes many routes
+    return ids
+
+
+@pytest.mark.parametrize("T,K,E,bs", [(100, 4, 8, 16), (1, 1, 4, 64), (4096, 8, 128, 64),
+                                      (37, 3, 7, 1), (0, 2, 5, 4), (513, 6, 256, 5),
+                                      (64, 8, 16, 128)])
+def test_permute_align(T, K, E, bs):
+    say(f"[align] T={T} K={K} E={E} bs={bs}")
+    ids = _ids(T, K, E, 1, hot=E - 1)
+    st, blk, num = B.moe_permute_align(ids, E, bs)
+    torch.cuda.synchronize()
+    st_o, blk_o, num_o = O.permute_align(ids.cpu().numpy(), E, bs)
+    assert int(num.item()) == num_o
+    assert np.array_equal(st.cpu().numpy(), st_o)
+    assert np.array_equal(blk.cpu().numpy(), blk_o)
+
+
+def _row_bits(t):
+    return t.view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+@pytest.mark.parametrize("layout,arg", [("contiguous", 1), ("contiguous", 16),
+                                        ("contiguous", 64), ("per_row", 8), ("per_row", 1),
+                                        ("masked", 40), ("masked", 512)])
+def test_pre_permute(dt, layout, arg):
+    T, K, E, H = 300, 4, 12, 136
+    say(f"[pre-permute] dt={dt} layout={layout} arg={arg}")
+    g = torch.Generator(device="cuda").manual_seed(2)
+    hidden = torch.randn((T, H), device="cuda", generator=g).to(DT[dt])
+    ids = _ids(T, K, E, 3, hot=5)
+    kw = {"max_m": arg} if layout == "masked" else {"block_size": arg}
+    x, meta, inv = B.moe_pre_permute(hidden, ids, E, layout, **kw)
+    torch.cuda.synchronize()
+    xo, meta_o, inv_o = O.pre_permute(np64(hidden), ids.cpu().numpy(), E, layout, **kw)
+    assert np.array_equal(meta.cpu().numpy(), meta_o)
+    assert np.array_equal(inv.cpu().numpy(), inv_o)
+    live = inv_o[inv_o >= 0]
+    got_rows = _row_bits(x.reshape(-1, H)[torch.as_tensor(live, device="cuda")])
+    want_rows = _row_bits(hidden[torch.as_tensor(np.nonzero(inv_o >= 0)[0] // K,
+                                                 device="cuda")])
+    assert np.array_equal(got_rows, want_rows)
+    if layout == "masked" and arg == 40:
+        assert (inv_o < 0).any()  # the hot expert overflowed its slab
+
+
+def _offsets_rows(sizes):
+    return np.concatenate([[0], np.cumsum(sizes)])
+
+
+LAYOUT_CASES = [("contiguous", 16), ("per_row", 8), ("masked", 160)]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("layout,arg", LAYOUT_CASES)
+@pytest.mark.parametrize("act", [None, "silu_and_mul", "swigluoai", "gelu_and_mul"])
+@pytest.mark.parametrize("bias", [False, True])
+def test_grouped_gemm_layout(dt, layout, arg, act, bias):
+    """Rows of the layout from moe_pre_permute; every computed row against the oracle;
+    rows of no expert keep the sentinel (per_row and masked; a contiguous segment's
+    padding is computed with its expert's weights)."""
+    T, K, E, H, N = 200, 3, 9, 264, 192  # ragged K tail (264 = 4*64 + 8), 1.5 N tiles
+    say(f"[gemm-layout] dt={dt} layout={layout} act={act} bias={bias}")
+    g = torch.Generator(device="cuda").manual_seed(4)
+    hidden = (2.0 * torch.randn((T, H), device="cuda", generator=g)).to(DT[dt])
+    ids = _ids(T, K, E, 5, hot=2)
+    kw = {"max_m": arg} if layout == "masked" else {"block_size": arg}
+    x, meta, inv = B.moe_pre_permute(hidden, ids, E, layout, **kw)
+    # rows the layout leaves unwritten hold whatever torch.empty gave: define them
+    xs = x.reshape(-1, H)
+    live = torch.zeros(xs.shape[0], dtype=torch.bool, device="cuda")
+    live[inv[inv >= 0].long()] = True
+    xs[~live] = 0
+    w = (0.1 * torch.randn((E, N, H), device="cuda", generator=g)).to(DT[dt])
+    bb = (0.3 * torch.randn((E, N), device="cuda", generator=g)).to(DT[dt]) if bias else None
+    Nout = N // 2 if act else N
+    out_shape = (E, arg, Nout) if layout == "masked" else (xs.shape[0], Nout)
+    out = torch.full(out_shape, SENTINEL, dtype=DT[dt], device="cuda")
+    B.moe_grouped_gemm_layout(x, w, layout, meta, bb, act, out=out)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm_layout(np64(x), LazyExperts(w), layout, meta.cpu().numpy(),
+                                None if bb is None else LazyExperts(bb), act, dt)
+    ref2, got2 = ref.reshape(-1, Nout), np64(out).reshape(-1, Nout)
+    own = ~np.isnan(ref2[:, 0])
+    assert own.sum() >= T * K * 0.5
+    assert_close(got2[own], ref2[own], dt, f"layout {layout} {act}")
+    if layout != "contiguous":
+        assert np.all(got2[~own] == SENTINEL)
+
+
+def test_grouped_gemm_layout_masked_clamps_counts():
+    """Counts past max_m read as max_m, negative ones as 0 (bf16, plain)."""
+    E, max_m, K, N = 4, 70, 128, 128
+    g = torch.Generator(device="cuda").manual_seed(6)
+    a = torch.randn((E, max_m, K), device="cuda", generator=g).to(torch.bfloat16)
+    w = (0.1 * torch.randn((E, N, K), device="cuda", generator=g)).to(torch.bfloat16)
+    counts = torch.tensor([500, -3, 0, 69], dtype=torch.int32, device="cuda")
+    out = torch.full((E, max_m, N), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    B.moe_grouped_gemm_layout(a, w, "masked", counts, out=out)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm_layout(np64(a), LazyExperts(w), "masked", counts.cpu().numpy(),
+                                None, None, "bf16")
+    got = np64(out)
+    own = ~np.isnan(ref[..., 0])
+    assert own.sum() == max_m + 69
+    assert_close(got[own], ref[own], "bf16", "masked clamp")
+    assert np.all(got[~own] == SENTINEL)
+
+
+@pytest.mark.parametrize("layout,arg", LAYOUT_CASES + [("masked", 20)])
+def test_layer_through_layout_ops(layout, arg):
+    """route -> pre_permute -> gate_up (SwiGLU) -> down -> combine over a layout equals the
+    oracle layer; with a small slab the routes without room contribute nothing."""
+    cfg = I.MoEConfig("layout_layer", T=256, H=256, E=16, F=128, K=4)
+    say(f"[layer-layout] {layout} {arg}")
+    d = I.make_inputs(cfg, device="cuda")
+    w, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize))
+    kw = {"max_m": arg} if layout == "masked" else {"block_size": arg}
+    x, meta, inv = B.moe_pre_permute(d["hidden"], ids, cfg.E, layout, **kw)
+    act = B.moe_grouped_gemm_layout(x, d["w_gate_up"], layout, meta, act="silu_and_mul")
+    y = B.moe_grouped_gemm_layout(act, d["w_down"], layout, meta)
+    out = B.moe_combine(y, w, inv)
+    torch.cuda.synchronize()
+    inv_np = inv.cpu().numpy()
+    ids_np = ids.cpu().numpy()
+    # oracle: the same routing, each route's expert MLP, dropped routes left out
+    h = np64(d["hidden"])
+    wts = w.cpu().numpy().astype(np.float64)
+    ref = np.zeros((cfg.T, cfg.H))
+    wgu, wd = LazyExperts(d["w_gate_up"]), LazyExperts(d["w_down"])
+    for e in range(cfg.E):
+        rr = np.nonzero((ids_np.reshape(-1) == e) & (inv_np >= 0))[0]
+        if rr.size == 0:
+            continue
+        _, ye = O.expert_mlp(h[rr // cfg.K], wgu[e], wd[e], act_dtype="bf16")
+        ye = O.round_to(ye, "bf16")
+        for q, r in enumerate(rr):
+            ref[r // cfg.K] += wts.reshape(-1)[r] * ye[q]
+    ref = O.round_to(ref, "bf16")
+    assert_close(np64(out), ref, "bf16", f"layer {layout}")
+    if layout == "masked" and arg == 20:
+        assert (inv_np < 0).any()
+
+
+def test_masked_bf16_gemm_full_size_sampled():
+    """The DeepSeek-V3 gate_up shape over a masked slab in bf16 (E 256, max_m 256, K 7168,
+    N 4096, about 128 rows per expert): every output on the GPU, sampled rows checked."""
+    cfg = I.FP8_CONFIGS["dsv3_fp8_gate_up"]
+    say("[gemm-layout-full] generating")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    a = torch.randn((cfg.E, cfg.max_m, cfg.K), device="cuda", generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn((cfg.E, cfg.N, cfg.K), device="cuda", generator=g)).to(
+        torch.bfloat16)
+    counts = I.fp8_counts(cfg, device="cuda")
+    out = torch.full((cfg.E, cfg.max_m, cfg.N), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    say("[gemm-layout-full] gemm")
+    B.moe_grouped_gemm_layout(a, w, "masked", counts, out=out)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    rng = np.random.default_rng(0)
+    for e in rng.choice(cfg.E, size=3, replace=False):
+        rows = np.sort(rng.choice(int(c[e]), size=4, replace=False))
+        ref = np64(a[e, rows]) @ np64(w[e]).T
+        assert_close(np64(out[e, rows]), O.round_to(ref, "bf16"), "bf16", f"expert {e}")
+        assert np.all(np64(out[e, int(c[e]):]) == SENTINEL)
