@@ -311,6 +311,101 @@ def swiglu_line(cfg, args):
     print(json.dumps(line), flush=True)
 
 
+def _timed_line(call, args, stream):
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    return ms_per_step, time_launches(call, args.kernel_reps, stream)
+
+
+def layout_line(cfg, args):
+    """Layout workloads: moe_pre_permute of a workload's routing into block-aligned rows
+    (value = routes per second), or the bf16 grouped GEMM over a masked slab (value =
+    valid rows / 8 per second, as the FP8 lines). Roofline against HBM."""
+    stream = torch.cuda.current_stream()
+    import oracle.moe_oracle as O
+    if cfg.kind == "pre_permute":
+        mc = I.CONFIGS[cfg.route]
+        d = I.make_inputs(mc, device="cuda")
+        _, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(mc.K, mc.scoring, mc.renormalize,
+                                                            mc.rsf, mc.G, mc.TG))
+        ws = torch.empty(B.moe_layout_workspace_size(mc.T, mc.K, mc.E, cfg.block_size),
+                         dtype=torch.uint8, device="cuda")
+        call = lambda: B.moe_pre_permute(d["hidden"], ids, mc.E, cfg.layout, cfg.block_size,
+                                         workspace=ws, stream=stream)
+        ms, k_ms = _timed_line(call, args, stream)
+        R = mc.T * mc.K
+        es = 4 if mc.dtype == "f32" else 2
+        k_bytes = mc.T * mc.H * es + R * mc.H * es + R * 4 + R * 4 + mc.E * 4
+        value, unit = R / (ms * 1e-3), "routes/s"
+        conf = {"workload": cfg.name, "T": mc.T, "top_k": mc.K, "E": mc.E, "H": mc.H,
+                "layout": cfg.layout, "block_size": cfg.block_size}
+        kernel = "permute + align + contiguous_rows_kernel (the whole op)"
+        dtype = mc.dtype
+        sample = None
+        if not args.no_cpu_baseline:
+            h = d["hidden"][:512].float().cpu().numpy().astype(np.float64)
+            ii = ids[:512].cpu().numpy()
+            done, total = 0, 0.0
+            while total < args.cpu_budget / 4:
+                t1 = time.perf_counter()
+                O.pre_permute(h, ii, mc.E, cfg.layout, cfg.block_size)
+                total += time.perf_counter() - t1
+                done += ii.size
+            sample = {"value": done / total, "unit": "routes/s", "cores": _blas_threads(),
+                      "kind": "oracle", "sample": f"first 512 of {mc.T} tokens ({ii.size} "
+                      f"routes), repeated, float64 numpy oracle, {total:.1f} s"}
+    else:
+        fc = I.FP8_CONFIGS[cfg.fp8]
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn((fc.E, fc.max_m, fc.K), device="cuda", generator=g).to(torch.bfloat16)
+        w = (cfg.w_std * torch.randn((fc.E, fc.N, fc.K), device="cuda", generator=g)).to(
+            torch.bfloat16)
+        counts = I.fp8_counts(fc, device="cuda")
+        out = torch.empty((fc.E, fc.max_m, fc.N), dtype=torch.bfloat16, device="cuda")
+        call = lambda: B.moe_grouped_gemm_layout(a, w, "masked", counts, out=out, stream=stream)
+        ms, k_ms = _timed_line(call, args, stream)
+        rows = int(counts.cpu().clamp(0, fc.max_m).sum())
+        k_bytes = fc.E * fc.N * fc.K * 2 + rows * fc.K * 2 + rows * fc.N * 2 + fc.E * 4
+        value, unit = rows / 8 / (ms * 1e-3), "tokens/s"
+        conf = {"workload": cfg.name, "E": fc.E, "max_m": fc.max_m, "K": fc.K, "N": fc.N,
+                "valid_rows": rows, "layout": "masked"}
+        kernel = "gemm_bf16_kernel (grouped GEMM, masked slab)"
+        dtype = "bf16"
+        sample = None
+        if not args.no_cpu_baseline:
+            cnt = counts.cpu().numpy()
+            done, total, e = 0, 0.0, 0
+            while total < args.cpu_budget / 2 and e < fc.E:
+                ae, we = a[e:e + 1].float().cpu().numpy(), w[e:e + 1].float().cpu().numpy()
+                t1 = time.perf_counter()
+                O.grouped_gemm_layout(ae, we, "masked", cnt[e:e + 1], None, None, "bf16")
+                total += time.perf_counter() - t1
+                done += int(cnt[e])
+                e += 1
+            sample = {"value": done / 8 / total, "unit": "tokens/s", "cores": _blas_threads(),
+                      "kind": "oracle", "sample": f"experts 0..{e - 1} of {fc.E} ({done} valid "
+                      f"rows), float64 numpy oracle, {total:.1f} s"}
+    achieved = k_bytes / (k_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded inputs)", "config": {**conf, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": kernel, "kernel_ms": round(k_ms, 5), "algorithmic_bytes": k_bytes},
+    }
+    if sample:
+        line["cpu_baseline"] = sample
+    print(json.dumps(line), flush=True)
+
+
 def fp8_line(cfg, args):
     """Block-scaled FP8 grouped GEMM over a masked slab (one step = one call). tokens =
     valid rows / 8 (the workload is the top-8 routed GEMM of T tokens)."""
@@ -433,7 +528,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="qwen3_bf16",
-                    choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS) + sorted(I.SWIGLU_CONFIGS))
+                    choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS) + sorted(I.SWIGLU_CONFIGS)
+                    + sorted(I.LAYOUT_CONFIGS))
     ap.add_argument("--backend", default="auto", choices=["auto", "staged", "indexed"])
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -456,6 +552,10 @@ def main():
     if args.workload in I.SWIGLU_CONFIGS:
         torch.cuda.set_device(0)
         swiglu_line(I.SWIGLU_CONFIGS[args.workload], args)
+        return
+    if args.workload in I.LAYOUT_CONFIGS:
+        torch.cuda.set_device(0)
+        layout_line(I.LAYOUT_CONFIGS[args.workload], args)
         return
     cfg = I.CONFIGS[args.workload]
     if cfg.H == 0:

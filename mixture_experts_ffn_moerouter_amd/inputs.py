@@ -346,3 +346,28 @@ def make_swiglu_inputs(cfg: SwigluConfig, *, seed: int = 0, device="cpu") -> dic
     return {"gate": normal((cfg.rows, 2 * cfg.F), cfg.x_std, seed=seed,
                            stream=STREAMS["hidden"], dtype=_TORCH_DT[cfg.dtype],
                            device=device)}
+
+
+# --------------------------------------------------------------------------------------
+# Layout workloads ([TO] MoEPrePermuteFwdOp, MoEGroupedGemmFwdOp's masked layout).
+
+@dataclass(frozen=True)
+class LayoutConfig:
+    name: str
+    kind: str                      # "pre_permute" or "masked_gemm"
+    route: Optional[str] = None    # pre_permute: the MoEConfig whose routing it permutes
+    layout: str = "contiguous"
+    block_size: int = 64
+    fp8: Optional[str] = None      # masked_gemm: the Fp8GemmConfig whose shapes it takes
+    w_std: float = 0.02
+
+
+LAYOUT_CONFIGS = {
+    # Qwen3 routing (T 4096, top-8 of 128) into block-aligned expert rows, block 64.
+    "qwen3_pre_permute_bs64": LayoutConfig("qwen3_pre_permute_bs64", "pre_permute",
+                                           route="qwen3_bf16"),
+    # The DeepSeek-V3 gate_up shape over a masked slab, in bfloat16 (the FP8 workload's
+    # shapes and counts).
+    "dsv3_bf16_masked_gate_up": LayoutConfig("dsv3_bf16_masked_gate_up", "masked_gemm",
+                                             layout="masked", fp8="dsv3_fp8_gate_up"),
+}
