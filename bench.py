@@ -375,7 +375,7 @@ def layout_line(cfg, args):
         value, unit = rows / 8 / (ms * 1e-3), "tokens/s"
         conf = {"workload": cfg.name, "E": fc.E, "max_m": fc.max_m, "K": fc.K, "N": fc.N,
                 "valid_rows": rows, "layout": "masked"}
-        kernel = "gemm_bf16_kernel (grouped GEMM, masked slab)"
+        kernel = "gemm_h16_kernel (grouped GEMM, masked slab)"
         dtype = "bf16"
         sample = None
         if not args.no_cpu_baseline:
@@ -594,7 +594,7 @@ def main():
         k_ms, _ = time_gate_up(cfg, d, args.kernel_reps)
         k_bytes = gate_up_algorithmic_bytes(cfg, n_exp)
         k_flops = gate_up_flops(cfg)
-        k_name = "gemm_bf16_kernel (grouped gate_up + SwiGLU)"
+        k_name = "gemm_h16_kernel (grouped gate_up + SwiGLU)"
         k_traffic = recorded_traffic(cfg.name)
     else:
         # decode: the two indexed kernels stream the touched experts' weights; the

@@ -11,31 +11,40 @@
 //      limit <= 0 disables both clamps. [TO] gelu_and_mul: gelu(gate) * up over stacked
 //      rows, read as the exact GELU x * Phi(x).
 //
-// 16-bit kernel (bfloat16 or float16 operands, the same tiles; only the MFMA and the
-// conversions differ), templated on the tile shape: RB and CB 32-row blocks of token rows and of
-// weight rows per wave, waves arranged WM x WN, so a tile is 32*RB*WM token rows x
-// 32*CB*WN weight rows, K in steps of 64 (v_mfma_f32_32x32x16_bf16, float32
-// accumulators); 128 x 128 and 128 x 256 are in use (see launch_bf16). The loop keeps
-// the loads of the next K steps in flight in registers (token rows PA steps ahead,
-// weights two) while the matrix cores work on the step held in LDS; LDS is double
-// buffered (row stride 72 elements: conflict-free 16-byte
-// fragment reads), and each load instruction reads whole 128-byte row segments. For the
-// gated activation the tile's weight rows are gate rows and the matching up rows, placed
-// so that a lane's gate and up accumulators hold the same output element; the epilogue
-// pairs them directly. Rows of A may be gathered (a_rows), so the permuted activation
-// copy is never materialised. Loads use buffer resources (32-bit offsets from a scalar
-// base); out-of-range pieces (rows past the tile, weight rows past N, the K tail, steps
-// past the end) get an offset past the buffer's range so the hardware returns zeros
-// without a branch, which keeps the compiler's wait counts of the pipeline exact.
+// 16-bit kernel (bfloat16 or float16 operands; only the MFMA and the conversions differ).
 //
-// Tile map: an expert with M_e rows gets ceil(M_e / (64*RB)) tiles of equal height
-// (rounded up to 32 rows); a wave's K loop is compiled for its count of live row blocks.
-// Tile counts come from expert_offsets on the device (no host synchronisation); the grid
-// is an upper bound, every workgroup rebuilds the map in LDS, picks its (tile, n-tile)
-// and leaves if it has none. Consecutive logical tiles go to the same XCD (workgroups are
-// dealt round-robin over the 8 XCDs) and are ordered expert, n-tile, row tile: the row
-// tiles sharing a weight slice run side by side on one L2, and so do the n-tiles sharing
-// the expert's token rows.
+// Tile: 128 token rows x 256 weight rows, eight waves (2 x 4) of 64 x 64; a K step is 64
+// elements, 128 bytes of every row. For the gated activation the tile's 256 weight rows
+// are the gate and up rows of 128 outputs, placed so that a wave's blocks j and j + 2
+// hold the gate and the up row of the same outputs; the epilogue pairs them directly.
+//
+// Staging. LDS holds a ring of NS stages (three; two when the contraction is a single
+// step) filled by direct-to-LDS buffer loads: no register staging and no LDS write
+// instructions. Step k + NS - 1 is requested while step k is multiplied. One load
+// instruction moves 1 KB, eight rows x 128 bytes (whole cache lines): lane l lands in row
+// l / 8, 16-byte slot l % 8, and fetches the row's piece (l % 8) ^ (row % 8), so slots
+// are XOR-swizzled by row. A wave's six transfers of a step (two of token rows, four of
+// weight rows) are spread through its MFMA stream. Rows of A may be gathered (a_rows),
+// so the permuted activation copy is never materialised. Out-of-range pieces (rows past
+// the tile, weight rows past N, the K tail, steps past the end) get an offset past the
+// buffer's range, so the hardware writes zeros without a branch. The compiler's
+// workgroup barrier would wait for every transfer in flight, so each step starts with an
+// explicit "own transfers of this step landed (vmcnt), own LDS reads done, barrier".
+//
+// Multiply. Fragments are read with lane (r, q) of a 16-row block taking pieces q and
+// q + 4 of row r (both operands alike, so products pair as in the plain sum); with the
+// XOR slots these reads are free of bank conflicts. Each 16 x 16 block takes two
+// v_mfma_f32_16x16x32 per step, weights as the first operand, so a lane's four results
+// are four consecutive outputs of one token row: one 8-byte store (16 in float32).
+//
+// Work. The grid is one workgroup per CU, each walking a list of tiles: the stage ring
+// runs across tile boundaries, so the next tile's first steps load during the current
+// tile's last steps and its epilogue. An expert with M_e rows gets ceil(M_e / 128) row
+// tiles of equal height (rounded up to 32 rows); the map is built on the device from the
+// layout metadata (no host synchronisation) and kept in LDS. Logical tiles are ordered
+// expert, n-tile, row tile and each XCD takes a contiguous range, its workgroups
+// striding through it together: the row tiles that share a weight slice run side by side
+// on one L2, and so do the n-tiles sharing the expert's token rows.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -44,33 +53,35 @@
 namespace moe {
 namespace {
 
-constexpr int kMaxE = 1024;
-constexpr int kXcd = 8;
-// Tile shape: RB 32-row blocks of token rows and CB 32-row blocks of weight rows per wave;
-// waves (wm, wn) are WM x WN, so a tile holds 32*RB*WM token rows and 32*CB*WN weight rows.
-// BK = K step; LDS rows are BK + 8 elements apart (16-byte fragment reads conflict-free).
-template <int RB, int CB, int BK, int NT, int WM> constexpr int stage_elems() {
-  return (32 * RB * WM + 32 * CB * (NT / 64 / WM)) * (BK + 8);
-}
-template <int RB, int CB, int BK, int NT, int WM, int NBUF>
-constexpr size_t lds_bytes() { return (size_t)NBUF * stage_elems<RB, CB, BK, NT, WM>() * 2; }
-constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
-
-
-__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
-}
-
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
-// 32 x 32 x 16 MFMA on eight 16-bit elements per lane: DT 1 bfloat16, 2 float16.
+constexpr int kNT = 512;                // 8 waves: 2 (token rows) x 4 (weight rows)
+constexpr int kBMX = 128;               // token rows per tile
+constexpr int kBNW = 256;               // weight rows per tile
+constexpr int kBK = 64;                 // K elements per step (128 bytes of a row)
+constexpr int kPA = kBMX / 64;          // 1 KB transfers per wave and step: token rows
+constexpr int kPB = kBNW / 64;          //   and weight rows
+constexpr int kPieces = kPA + kPB;
+constexpr int kStage = (kBMX + kBNW) * 128;
+constexpr int kMaxE = 1024;
+constexpr int kMapBytes = 3 * (kMaxE + 1) * (int)sizeof(int);
+constexpr int kXcd = 8;
+constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
+static_assert(3 * kStage + kMapBytes <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
+// 16 x 16 x 32 MFMA on eight 16-bit elements per lane: DT 1 bfloat16, 2 float16.
 template <int DT>
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   if constexpr (DT == 2)
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                    __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   else
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // The gated activation of the epilogue: kind 1 gelu_and_mul, else the swiglu family.
@@ -79,294 +90,281 @@ __device__ __forceinline__ float gated_f(int kind, float g, float l, float alpha
   return kind == 1 ? gelu_f(g) * l : swiglu_f(g, l, alpha, beta, limit);
 }
 
-template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
-          int LAYOUT, bool OUT_F32, int DT>
-__global__ __launch_bounds__(NT, OCC) void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int LDK = BK + 8, CPR = BK / 8, RSTEP = NT / CPR;  // 16-byte pieces per row
-  constexpr int WN = NT / 64 / WM;  // waves: WM along the token rows x WN along the weights
-  constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * WN;
-  constexpr int NLD = (BMX * BK / 8) / NT, NLDB = (BNW * BK / 8) / NT;
-  constexpr int kStageElems = stage_elems<RB, CB, BK, NT, WM>();
-  static_assert(lds_bytes<RB, CB, BK, NT, WM, NBUF>() >= 3 * (kMaxE + 1) * sizeof(int),
-                "tile map alias");
-  static_assert(NBUF == 2 || PA == 1, "one LDS buffer goes with A one step ahead");
-  static_assert(NBUF == 2 || MID >= BK / 16, "one LDS buffer: the store follows the last MFMA");
-  static_assert(CB == 2 || CB == 4, "weight blocks per wave");
-  __shared__ int s_tmp[NT / 64];
-  extern __shared__ __align__(16) uint16_t smem[];  // [2][BMX + BNW][LDK]
-  int* s_start = (int*)smem;  // the tile map lives in the stage buffers until the K loop
+template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT>
+__global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
+  constexpr int LA = NS - 1;  // steps in flight ahead of the one multiplied
+  __shared__ int s_tmp[kNT / 64];
+  extern __shared__ __align__(16) uint8_t smem[];  // [NS][kStage], then the tile map
+  int* s_start = (int*)(smem + NS * kStage);
   int* s_len = s_start + kMaxE + 1;
   int* s_pre = s_len + kMaxE + 1;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = g.E;
-  build_tile_map_segments<NT>(g.seg_mode, g.offsets, E, g.M, g.max_m, BMX, s_start, s_len,
-                              s_pre, s_tmp);
-
-  const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
+  build_tile_map_segments<kNT>(g.seg_mode, g.offsets, E, g.M, g.max_m, kBMX, s_start, s_len,
+                               s_pre, s_tmp);
+  const int n_tiles_n = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
   const int n_valid = s_pre[E] * n_tiles_n;
+  // XCD x (workgroups b with b % 8 == x) owns logical tiles [x per, (x + 1) per); its
+  // workgroups take them in turn, so at any time they hold a contiguous run.
   const int per = (n_valid + kXcd - 1) / kXcd;
-  const int slot = blockIdx.x / kXcd;
-  const int L = (blockIdx.x % kXcd) * per + slot;
-  if (slot >= per || L >= n_valid) return;  // uniform per workgroup
-  // Logical order: expert, then n-tile, then row tile, so the row tiles that share one
-  // weight slice are adjacent (they run side by side on one XCD and the weight lines are
-  // fetched from HBM once); expert e owns [s_pre[e], s_pre[e+1]) * n_tiles_n.
-  const int e = find_expert(s_pre, E, L / n_tiles_n);
-  const int t_e = s_pre[e + 1] - s_pre[e];
-  const int local = L - s_pre[e] * n_tiles_n;
-  const int nt = local / t_e, mt = local % t_e;
-  const int rpt = rows_per_tile(s_len[e], BMX);
-  const int m0 = s_start[e] + mt * rpt;
-  const int m1 = min(m0 + rpt, s_start[e] + s_len[e]);
-  const int rows = m1 - m0;
-  const int nb = (rows + 31) / 32;  // live 32-row blocks
-  const int Kd = g.Kd;
-  __syncthreads();  // every thread has read the map; the buffers become stages
+  const int xcd = blockIdx.x % kXcd, nslot = gridDim.x / kXcd;
+  const int L0 = xcd * per + blockIdx.x / kXcd;
+  const int Lend = min((xcd + 1) * per, n_valid);
+  if (L0 >= Lend) return;  // uniform per workgroup
+  const int ntile = (Lend - L0 + nslot - 1) / nslot;
+  const int Kd = g.Kd, nk = (Kd + kBK - 1) / kBK;
 
-  // ---- loads: thread tid moves 16-byte piece tid % CPR of rows tid / CPR + RSTEP i, i < NLD,
-  // of both the A and the B tile (CPR consecutive lanes read one row segment).
-  const int kc = (tid % CPR) * 8;
+  // i-th tile of this workgroup: expert, n-tile, rows [m0, m1)
+  auto tile = [&](int i, int& e, int& nt, int& m0, int& m1) {
+    const int L = L0 + i * nslot;
+    e = __builtin_amdgcn_readfirstlane(find_expert(s_pre, E, L / n_tiles_n));
+    const int t_e = s_pre[e + 1] - s_pre[e];
+    const int local = L - s_pre[e] * n_tiles_n;
+    nt = __builtin_amdgcn_readfirstlane(local / t_e);
+    const int rpt = rows_per_tile(s_len[e], kBMX);
+    m0 = __builtin_amdgcn_readfirstlane(s_start[e] + (local % t_e) * rpt);
+    m1 = __builtin_amdgcn_readfirstlane(min(m0 + rpt, s_start[e] + s_len[e]));
+  };
+
+  // Transfers: wave w moves 1 KB pieces kPA w + u of the token rows (rows 16 w .. 16 w + 15)
+  // and kPB w + u of the weight rows (rows 32 w .. 32 w + 31); lane l takes row l / 8 of
+  // the piece and its 16-byte part (l % 8) ^ (row % 8).
+  const int prow = lane >> 3;
+  const int kel = 8 * ((lane & 7) ^ prow);  // first K element of the lane's part
+  const uint32_t pbyte = 2u * (uint32_t)kel;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, 0x7fffffff, 0x00020000);
-  const uint16_t* Bexp = (const uint16_t*)g.b + (int64_t)e * g.Nw * Kd;
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Bexp, (short)0, (int)((int64_t)g.Nw * Kd * 2), 0x00020000);
-  uint32_t aoff[NLD], boff[NLDB];
+  // per-lane byte offsets (and the expert's weight buffer) of one tile
+  auto offsets = [&](int e, int nt, int m0, int m1, uint32_t* ao, uint32_t* bo,
+                     __amdgpu_buffer_rsrc_t& rb) {
+    const int rows = m1 - m0;
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int r = tid / CPR + RSTEP * i;
-    const bool aon = r < rows;
-    const int m = m0 + (aon ? r : 0);
-    const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
-    aoff[i] = aon ? ((uint32_t)src * (uint32_t)Kd + kc) * 2u : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < NLDB; ++i) {
-    const int r = tid / CPR + RSTEP * i;
-    int wr;
-    bool bon;
-    if (ACT) {
-      const int j = nt * (BNW / 2) + (r & (BNW / 2 - 1));
-      const bool up = r >= BNW / 2;
-      bon = j < g.Nout;
-      wr = LAYOUT == 0 ? (up ? g.Nout + j : j) : (2 * j + (up ? 1 : 0));
-    } else {
-      wr = nt * BNW + r;
-      bon = wr < g.Nw;
+    for (int u = 0; u < kPA; ++u) {
+      const int r = 8 * (kPA * wave + u) + prow;
+      const bool on = r < rows;
+      const int m = m0 + (on ? r : 0);
+      const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
+      ao[u] = on ? (uint32_t)src * (uint32_t)Kd * 2u + pbyte : kOOB;
     }
-    boff[i] = bon ? ((uint32_t)wr * (uint32_t)Kd + kc) * 2u : kOOB;
-  }
-
-  // A (token rows, mostly from L2) is prefetched PA K steps ahead, the weights (from HBM)
-  // two: sa0/sa1 hold A of the next step(s), sb0/sb1 the weights of the next two.
-  bf16x8 sa0[NLD], sa1[PA == 2 ? NLD : 1], sb0[NLDB], sb1[NLDB];
-  auto load_a = [&](int k0, bf16x8* xa) {
-    const bool kin = k0 + kc < Kd;
+    rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)g.b + (int64_t)e * g.Nw * Kd), (short)0,
+        (int)((int64_t)g.Nw * Kd * 2), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) xa[i] = buf_load16(ra, kin ? aoff[i] + 2u * (uint32_t)k0 : kOOB);
-  };
-  auto load_b = [&](int k0, bf16x8* xb) {
-    const bool kin = k0 + kc < Kd;
-#pragma unroll
-    for (int i = 0; i < NLDB; ++i) xb[i] = buf_load16(rb, kin ? boff[i] + 2u * (uint32_t)k0 : kOOB);
-  };
-  auto store_stage = [&](int buf, const bf16x8* xa, const bf16x8* xb) {
-    uint16_t* la = smem + buf * kStageElems;
-    uint16_t* lb = la + BMX * LDK;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) *(bf16x8*)(la + (tid / CPR + RSTEP * i) * LDK + kc) = xa[i];
-#pragma unroll
-    for (int i = 0; i < NLDB; ++i) *(bf16x8*)(lb + (tid / CPR + RSTEP * i) * LDK + kc) = xb[i];
-  };
-
-  // wave (wm, wn): row blocks wm, wm+WM, ... (RB of them); weight rows: for the gated
-  // activation gate rows wn*16*CB + [0,16*CB) and the matching up rows BNW/2 + the same;
-  // else wn*32*CB + [0,32*CB).
-  const int wm = wave % WM, wn = wave / WM;
-  int brow[CB];
-#pragma unroll
-  for (int j = 0; j < CB; ++j)
-    brow[j] = (ACT ? ((j / (CB / 2)) * (BNW / 2) + wn * 16 * CB + (j % (CB / 2)) * 32)
-                   : (wn * 32 * CB + j * 32)) +
-              (lane & 31);
-  const int kq = (lane >> 5) * 8;
-  const int nbw = nb > wm ? (nb - wm + WM - 1) / WM : 0;  // live row blocks of this wave
-
-  f32x16 acc[RB][CB];
-#pragma unroll
-  for (int i = 0; i < RB; ++i)
-#pragma unroll
-    for (int j = 0; j < CB; ++j) acc[i][j] = f32x16{};
-
-  // The K loop, compiled once per count of live row blocks so that every fragment read
-  // of a sub-step is issued before its MFMAs.
-  auto main_loop = [&](auto nbw_c) {
-    constexpr int NBW = decltype(nbw_c)::value;
-    // compute(buf, mid): the MFMAs of one K step from LDS buffer buf; mid() (the store of
-    // the next step and the loads two steps ahead) runs after sub-step MID - 1, pinned
-    // there, so those waits and LDS writes overlap the remaining MFMAs (MID = BK/16: at
-    // the end).
-    auto compute = [&](int buf, auto&& mid) {
-      const uint16_t* sa = smem + buf * kStageElems;
-      const uint16_t* sb = sa + BMX * LDK;
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        if (ks == MID) {
-          __builtin_amdgcn_sched_barrier(0);
-          mid();
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        bf16x8 fb[CB], fa[NBW];
-#pragma unroll
-        for (int j = 0; j < CB; ++j) fb[j] = *(const bf16x8*)(sb + brow[j] * LDK + ks * 16 + kq);
-#pragma unroll
-        for (int i = 0; i < NBW; ++i)
-          fa[i] = *(const bf16x8*)(sa + ((wm + WM * i) * 32 + (lane & 31)) * LDK + ks * 16 + kq);
-#pragma unroll
-        for (int i = 0; i < NBW; ++i)
-#pragma unroll
-          for (int j = 0; j < CB; ++j)
-            acc[i][j] = mfma32<DT>(fa[i], fb[j], acc[i][j]);
+    for (int u = 0; u < kPB; ++u) {
+      const int b = 8 * (kPB * wave + u) + prow;  // weight row of the tile
+      int wr;
+      bool on;
+      if (ACT) {  // wave b / 64, block (b / 16) % 4: gate rows (blocks 0, 1), up rows (2, 3)
+        const int j = (b >> 4) & 3;
+        const int o = nt * (kBNW / 2) + (b >> 6) * 32 + 16 * (j & 1) + (b & 15);
+        const bool up = j >= 2;
+        on = o < g.Nout;
+        wr = LAYOUT == 0 ? (up ? g.Nout + o : o) : (2 * o + (up ? 1 : 0));
+      } else {
+        wr = nt * kBNW + b;
+        on = wr < g.Nw;
       }
-      if (MID >= BK / 16) mid();
-    };
-    auto none = [] {};
-    // Step s uses LDS buffer s % 2 and weight set sb[s % 2] (and, with PA = 2, A set
-    // sa[s % 2]). After storing step k+1 the loads of the steps two ahead (PA = 2: A and
-    // weights of k+3) or A of k+2 and then the weights of k+3 (PA = 1) are issued, so the
-    // wait before the next store leaves the newest loads in flight. Every half-iteration
-    // issues the same loads (steps past the end load nothing: their offsets are out of
-    // range), which keeps the compiler's wait counts exact.
-    const int nk = (Kd + BK - 1) / BK;
-    int k = 0;
-    if constexpr (PA == 2) {
-      load_a(0, sa0);
-      load_b(0, sb0);
-      load_a(BK, sa1);
-      load_b(BK, sb1);
-      store_stage(0, sa0, sb0);
-      load_a(2 * BK, sa0);
-      load_b(2 * BK, sb0);
-      __syncthreads();
-      for (; k + 1 < nk; k += 2) {
-        compute(0, [&] {
-          store_stage(1, sa1, sb1);
-          load_a((k + 3) * BK, sa1);
-          load_b((k + 3) * BK, sb1);
-        });
-        __syncthreads();
-        compute(1, [&] {
-          store_stage(0, sa0, sb0);
-          load_a((k + 4) * BK, sa0);
-          load_b((k + 4) * BK, sb0);
-        });
-        __syncthreads();
-      }
-    } else {
-      // With one LDS buffer (NBUF == 1) every step ends with a barrier before the store
-      // that overwrites it, and a barrier after.
-      constexpr int B1 = NBUF == 2 ? 1 : 0;
-      load_a(0, sa0);
-      load_b(0, sb0);
-      load_b(BK, sb1);
-      store_stage(0, sa0, sb0);
-      load_a(BK, sa0);
-      load_b(2 * BK, sb0);
-      __syncthreads();
-      for (; k + 1 < nk; k += 2) {
-        compute(0, [&] {
-          if (NBUF == 1) __syncthreads();
-          store_stage(B1, sa0, sb1);
-          load_a((k + 2) * BK, sa0);
-          load_b((k + 3) * BK, sb1);
-        });
-        __syncthreads();
-        compute(B1, [&] {
-          if (NBUF == 1) __syncthreads();
-          store_stage(0, sa0, sb0);
-          load_a((k + 3) * BK, sa0);
-          load_b((k + 4) * BK, sb0);
-        });
-        __syncthreads();
-      }
+      bo[u] = on ? (uint32_t)wr * (uint32_t)Kd * 2u + pbyte : kOOB;
     }
-    if (k < nk) compute(0, none);  // odd number of K steps: the last one is in buffer 0
   };
-  // With 128-row tiles the loop is compiled for 2 and for 1 live row blocks of the wave;
-  // with 256-row tiles one loop covers all 4 (blocks past the tile's last row read rows
-  // that load as zeros, and their results are not written).
-  if constexpr (RB == 2) {
-    if (nbw >= 2) main_loop(std::integral_constant<int, 2>{});
-    else main_loop(std::integral_constant<int, 1>{});
-  } else if constexpr (RB == 4 && CB == 2) {
-    if (nbw >= 3) main_loop(std::integral_constant<int, 4>{});
-    else main_loop(std::integral_constant<int, 2>{});
-  } else {
-    main_loop(std::integral_constant<int, RB>{});
-  }
+  int te, tnt, tm0, tm1;              // the tile being multiplied
+  uint32_t aC[kPA], bC[kPB], aN[kPA], bN[kPB];  // offsets of this tile and the next
+  __amdgpu_buffer_rsrc_t rbC, rbN;
+  tile(0, te, tnt, tm0, tm1);
+  offsets(te, tnt, tm0, tm1, aC, bC, rbC);
+  // transfer p of step kk of this tile (nxt false) or the next into stage st
+  auto piece = [&](int stage, int kk, bool nxt, int p) {
+    uint8_t* st = smem + stage * kStage;
+    const int k0 = kk * kBK;
+    const bool in = k0 + kel < Kd;
+    const uint32_t kbyte = (uint32_t)k0 * 2u;
+    if (p < kPA) {
+      const uint32_t o = nxt ? aN[p] : aC[p];
+      dma16(ra, st + (kPA * wave + p) * 1024, in ? o + kbyte : kOOB);
+    } else {
+      const uint32_t o = nxt ? bN[p - kPA] : bC[p - kPA];
+      dma16(nxt ? rbN : rbC, st + kBMX * 128 + (kPB * wave + p - kPA) * 1024,
+            in ? o + kbyte : kOOB);
+    }
+  };
 
-  // ---- epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4
-  // and column l%32 of its 32 x 32 block.
+  // Wave (wm, wn): token 16-row blocks rowblk(i) = (wm + 2 (i / 2)) 32 + 16 (i % 2), weight
+  // rows wn 64 + 16 j. Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lr = lane & 15, lq = lane >> 4;
+  const uint32_t fo0 = 16u * (uint32_t)(lq ^ (lr & 7));
+  const uint32_t fo1 = 16u * (uint32_t)((lq ^ 4) ^ (lr & 7));
+  auto rowblk = [&](int i) { return (wm + 2 * (i >> 1)) * 32 + 16 * (i & 1); };
+
+#pragma unroll
+  for (int q = 0; q < LA; ++q)
+#pragma unroll
+    for (int p = 0; p < kPieces; ++p) piece(q, q, false, p);
+
   const uint16_t* bias = (const uint16_t*)g.bias;
-  if (ACT) {
+  const bool aligned = ((uintptr_t)g.out & 15) == 0;
+  int gs = 0;  // steps of the earlier tiles (ring position)
+  for (int ti = 0; ti < ntile; ++ti) {
+    if (ti + 1 < ntile) {
+      int e2, nt2, m02, m12;
+      tile(ti + 1, e2, nt2, m02, m12);
+      offsets(e2, nt2, m02, m12, aN, bN, rbN);
+    } else {  // the ring's last transfers move nothing
 #pragma unroll
-    for (int h = 0; h < CB / 2; ++h) {  // 32-column groups of this wave's 16*CB outputs
-      const int j = nt * (BNW / 2) + wn * 16 * CB + h * 32 + (lane & 31);
-      if (j < g.Nout) {
-        float bg = 0.f, bu = 0.f;
-        if (bias) {
-          const uint16_t* be = bias + (int64_t)e * g.Nw;
-          bg = h16_to_f32<DT>(be[LAYOUT == 0 ? j : 2 * j]);
-          bu = h16_to_f32<DT>(be[LAYOUT == 0 ? g.Nout + j : 2 * j + 1]);
+      for (int u = 0; u < kPA; ++u) aN[u] = kOOB;
+#pragma unroll
+      for (int u = 0; u < kPB; ++u) bN[u] = kOOB;
+      rbN = rbC;
+    }
+    const int e = te, nt = tnt, m0 = tm0, m1 = tm1;
+    const int nb = (m1 - m0 + 31) / 32;               // live 32-row blocks of the tile
+    const int nbw = nb > wm ? (nb - wm + 1) / 2 : 0;  // ... and of this wave
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
+
+    // The K loop, compiled for 4 and for 2 live 16-row blocks of the wave.
+    auto main_loop = [&](auto ni_c) {
+      constexpr int NI = decltype(ni_c)::value;
+      constexpr int NB = NI * 8;  // MFMAs per step
+      constexpr int EVERY = NB / kPieces;
+      static_assert(EVERY >= 1 && EVERY * kPieces <= NB, "every transfer is issued");
+      for (int k = 0; k < nk; ++k) {
+        // This wave's transfers of step k have landed (the newer LA - 1 steps' may not
+        // have) and its reads of step k - 1 are done; after the barrier every wave's are,
+        // so stage s % NS is complete and stage (s + LA) % NS is free.
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((LA - 1) * kPieces)
+                     : "memory");
+        const int s = gs + k;
+        const uint8_t* st = smem + (s % NS) * kStage;
+        const uint8_t* sb = st + kBMX * 128;
+        const int s2 = (s + LA) % NS;
+        const bool nxt = k + LA >= nk;
+        const int kk = nxt ? k + LA - nk : k + LA;
+        bf16x8 fa[NI][2], fb[4][2];
+        auto rd = [&](bf16x8* f, const uint8_t* rowp) {
+          f[0] = *(const bf16x8*)(rowp + fo0);
+          f[1] = *(const bf16x8*)(rowp + fo1);
+        };
+        // every operand of the step, in the order the MFMAs consume them
+        rd(fa[0], st + (rowblk(0) + lr) * 128);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rd(fb[j], sb + (wn * 64 + 16 * j + lr) * 128);
+          __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          if (i < nbw) {
-            const int rb = wm + WM * i;
+        for (int i = 1; i < NI; ++i) {
+          rd(fa[i], st + (rowblk(i) + lr) * 128);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // MFMA t and, every EVERY-th slot, one transfer of step s + LA (pinned in order)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-              if (m < m1) {
-                float v = gated_f(g.act_kind, acc[i][h][r] + bg, acc[i][CB / 2 + h][r] + bu,
-                                  g.alpha, g.beta, g.limit);
-                if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nout + j] = v;
-                else ((uint16_t*)g.out)[(int64_t)m * g.Nout + j] = f32_to_h16<DT>(v);
-              }
+        for (int t = 0; t < NB; ++t) {
+          const int c = t / (NI * 4), u = t % (NI * 4), i = u / 4, j = u % 4;
+          acc[i][j] = mfma16<DT>(fb[j][c], fa[i][c], acc[i][j]);
+          if (t % EVERY == EVERY - 1 && t / EVERY < kPieces) piece(s2, kk, nxt, t / EVERY);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    if (nbw >= 2) main_loop(std::integral_constant<int, 4>{});
+    else main_loop(std::integral_constant<int, 2>{});
+    gs += nk;
+
+    // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
+    // wn 64 + 16 j + 4 q .. + 3.
+    auto store4 = [&](int64_t idx, const float* v, bool vec, int n, int nmax) {
+      if (vec) {
+        if (OUT_F32) {
+          *(f32x4*)((float*)g.out + idx) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          const uint32_t lo =
+              (uint32_t)f32_to_h16<DT>(v[0]) | ((uint32_t)f32_to_h16<DT>(v[1]) << 16);
+          const uint32_t hi =
+              (uint32_t)f32_to_h16<DT>(v[2]) | ((uint32_t)f32_to_h16<DT>(v[3]) << 16);
+          *(uint2*)((uint16_t*)g.out + idx) = make_uint2(lo, hi);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (n + c < nmax) {
+            if (OUT_F32) ((float*)g.out)[idx + c] = v[c];
+            else ((uint16_t*)g.out)[idx + c] = f32_to_h16<DT>(v[c]);
+          }
+        }
+      }
+    };
+    if (ACT) {
+      const bool vrow = (g.Nout & 3) == 0 && aligned;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int o0 = nt * (kBNW / 2) + wn * 32 + 16 * j + 4 * lq;
+        if (o0 < g.Nout) {
+          float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            const uint16_t* be = bias + (int64_t)e * g.Nw;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const int o = min(o0 + c, g.Nout - 1);
+              bg[c] = h16_to_f32<DT>(be[LAYOUT == 0 ? o : 2 * o]);
+              bu[c] = h16_to_f32<DT>(be[LAYOUT == 0 ? g.Nout + o : 2 * o + 1]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + rowblk(i) + lr;
+            if (i < 2 * nbw && m < m1) {
+              float v[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                v[c] = gated_f(g.act_kind, acc[i][j][c] + bg[c], acc[i][j + 2][c] + bu[c],
+                               g.alpha, g.beta, g.limit);
+              store4((int64_t)m * g.Nout + o0, v, vrow && o0 + 3 < g.Nout, o0, g.Nout);
+            }
+          }
+        }
+      }
+    } else {
+      const bool vrow = (g.Nw & 3) == 0 && aligned;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n0 = nt * kBNW + wn * 64 + 16 * j + 4 * lq;
+        if (n0 < g.Nw) {
+          float bn[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              bn[c] = h16_to_f32<DT>(bias[(int64_t)e * g.Nw + min(n0 + c, g.Nw - 1)]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = m0 + rowblk(i) + lr;
+            if (i < 2 * nbw && m < m1) {
+              float v[4];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) v[c] = acc[i][j][c] + bn[c];
+              store4((int64_t)m * g.Nw + n0, v, vrow && n0 + 3 < g.Nw, n0, g.Nw);
             }
           }
         }
       }
     }
-  } else {
+    if (ti + 1 < ntile) tile(ti + 1, te, tnt, tm0, tm1);
 #pragma unroll
-    for (int jb = 0; jb < CB; ++jb) {
-      const int n = nt * BNW + wn * 32 * CB + jb * 32 + (lane & 31);
-      if (n < g.Nw) {
-        const float bn = bias ? h16_to_f32<DT>(bias[(int64_t)e * g.Nw + n]) : 0.f;
+    for (int u = 0; u < kPA; ++u) aC[u] = aN[u];
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          if (i < nbw) {
-            const int rb = wm + WM * i;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int m = m0 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-              if (m < m1) {
-                float v = acc[i][jb][r] + bn;
-                if (OUT_F32) ((float*)g.out)[(int64_t)m * g.Nw + n] = v;
-                else ((uint16_t*)g.out)[(int64_t)m * g.Nw + n] = f32_to_h16<DT>(v);
-              }
-            }
-          }
-        }
-      }
-    }
+    for (int u = 0; u < kPB; ++u) bC[u] = bN[u];
+    rbC = rbN;
   }
+  // no transfer into LDS may outlive the workgroup
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// float32 operands: one workgroup per output row; the A row is staged in LDS and each
-// thread forms the dot products of its output column(s). Plain FMA arithmetic; meant
-// for small float32 problems.
 // Expert owning row m under the segment metadata of g (see GemmArgs), or -1.
 __device__ int row_owner(const GemmArgs& g, int m) {
   const int32_t* meta = g.offsets;
@@ -431,49 +429,57 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-template <int RB, int CB, int PA, int BK, int NT, int WM, int OCC, int MID, int NBUF, bool ACT,
-          int LAYOUT, bool OUT_F32, int DT>
-hipError_t launch_bf16_shape(const GemmArgs& g, hipStream_t s) {
-  constexpr int BMX = 32 * RB * WM, BNW = 32 * CB * (NT / 64 / WM);
-  const int n_tiles_n = ACT ? (g.Nout + BNW / 2 - 1) / (BNW / 2) : (g.Nw + BNW - 1) / BNW;
-  const int64_t max_tiles = (g.M + BMX - 1) / BMX + (g.E < g.M ? g.E : g.M);
+
+int cu_count() {
+  static int n = 0;  // per process; every device used here has the same count
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
+template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT>
+hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
+  const int n_tiles_n = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
+  const int64_t max_tiles = ((int64_t)g.M + kBMX - 1) / kBMX + (g.E < g.M ? g.E : g.M);
   int64_t grid = max_tiles * n_tiles_n;
-  grid = (grid + kXcd - 1) / kXcd * kXcd;
-  const auto kern = gemm_bf16_kernel<RB, CB, PA, BK, NT, WM, OCC, MID, NBUF, ACT, LAYOUT, OUT_F32, DT>;
+  const int64_t cap = cu_count() / kXcd * kXcd;  // one workgroup per CU
+  if (grid > cap) grid = cap;
+  grid = (grid + kXcd - 1) / kXcd * kXcd;       // a multiple of the XCD count
+  const size_t lds = (size_t)NS * kStage + kMapBytes;
+  const auto kern = gemm_h16_kernel<NS, ACT, LAYOUT, OUT_F32, DT>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds_bytes<RB, CB, BK, NT, WM, NBUF>());
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  kern<<<dim3((unsigned)grid), dim3(NT), lds_bytes<RB, CB, BK, NT, WM, NBUF>(), s>>>(g);
+  kern<<<dim3((unsigned)grid), dim3(kNT), lds, s>>>(g);
   return hipGetLastError();
 }
 
-// Two shapes, chosen by the contraction length. Long contractions (Kd >= 2560) take 128
-// token rows x 256 weight rows per workgroup, eight waves (2 x 4) of 64 x 64, one
-// workgroup per CU: half as many n-tiles re-read each expert's token rows per weight
-// byte. Shorter ones take 128 x 128 with four waves and two workgroups per CU, where one
-// workgroup's prologue and epilogue overlap the other's K loop. Both keep the two
-// operands two K steps ahead. Measured in one process, alternating the shapes: 5% and 3%
-// faster layers with the wide tile at Kd 7168 and 2880, 2% slower at Kd 2048 / 768.
+// Three stages (two steps in flight) need at least two steps per tile; a single-step
+// contraction runs with two.
 template <bool ACT, int LAYOUT, bool OUT_F32, int DT>
-hipError_t launch_bf16(const GemmArgs& g, hipStream_t s) {
-  // <RB, CB, PA, BK, NT, WM, OCC, MID, NBUF>
-  if (g.Kd >= 2560)
-    return launch_bf16_shape<2, 2, 2, 64, 512, 2, 1, 4, 2, ACT, LAYOUT, OUT_F32, DT>(g, s);
-  return launch_bf16_shape<2, 2, 2, 64, 256, 2, 2, 4, 2, ACT, LAYOUT, OUT_F32, DT>(g, s);
+hipError_t launch_h16_act(const GemmArgs& g, hipStream_t s) {
+  if (g.Kd > kBK) return launch_h16_ns<3, ACT, LAYOUT, OUT_F32, DT>(g, s);
+  return launch_h16_ns<2, ACT, LAYOUT, OUT_F32, DT>(g, s);
 }
 
 template <int DT>
 hipError_t launch_h16(const GemmArgs& g, hipStream_t s) {
   if (g.act) {
     if (g.layout == 0)
-      return g.out_dt == 0 ? launch_bf16<true, 0, true, DT>(g, s)
-                           : launch_bf16<true, 0, false, DT>(g, s);
-    return g.out_dt == 0 ? launch_bf16<true, 1, true, DT>(g, s)
-                         : launch_bf16<true, 1, false, DT>(g, s);
+      return g.out_dt == 0 ? launch_h16_act<true, 0, true, DT>(g, s)
+                           : launch_h16_act<true, 0, false, DT>(g, s);
+    return g.out_dt == 0 ? launch_h16_act<true, 1, true, DT>(g, s)
+                         : launch_h16_act<true, 1, false, DT>(g, s);
   }
-  return g.out_dt == 0 ? launch_bf16<false, 0, true, DT>(g, s)
-                       : launch_bf16<false, 0, false, DT>(g, s);
+  return g.out_dt == 0 ? launch_h16_act<false, 0, true, DT>(g, s)
+                       : launch_h16_act<false, 0, false, DT>(g, s);
 }
 
 }  // namespace
