@@ -6,12 +6,17 @@
 //      any layout's inverse index; a negative entry (a route a masked slab had no room
 //      for) contributes nothing.
 //
-// One workgroup per token; each thread owns 8 consecutive hidden elements (16-byte
-// loads of 16-bit rows), sums its K rows in float32 in k order and writes once.
+// One workgroup per token and chunk of kChunk hidden elements (several per token when H is
+// large, so small batches still spread over the chip); each thread owns 8 consecutive
+// elements (16-byte loads of 16-bit rows), sums its K rows in float32 in k order and
+// writes once.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = kThreads * 8;  // hidden elements per workgroup
 
 // Eight elements of y (dtype YDT: 0 f32, 1 bf16, 2 f16) as float32.
 template <int YDT>
@@ -31,7 +36,7 @@ __device__ __forceinline__ void load8(const void* p, float* v) {
 }
 
 template <int YDT, bool VEC>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y,
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ route_pos,
                                                       int T, int K, int H, float scale,
@@ -41,8 +46,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   const float* wt = w + (int64_t)t * K;
   const int32_t* pt = route_pos + (int64_t)t * K;
   const int ysz = YDT == 0 ? 4 : 2;
+  const int h_end = min(H, (int)(blockIdx.y + 1) * kChunk);
   if (VEC) {
-    for (int h = threadIdx.x * 8; h < H; h += blockDim.x * 8) {
+    for (int h = blockIdx.y * kChunk + threadIdx.x * 8; h < h_end; h += kChunk) {
       float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       for (int k = 0; k < K; ++k) {
         if (pt[k] < 0) continue;  // a route without a row contributes nothing
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
       }
     }
   } else {
-    for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    for (int h = blockIdx.y * kChunk + threadIdx.x; h < h_end; h += kThreads) {
       float acc = 0.f;
       for (int k = 0; k < K; ++k) {
         if (pt[k] < 0) continue;
@@ -84,11 +90,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 hipError_t launch_combine(const void* y, int y_dt, const float* w, const int32_t* route_pos,
                           int T, int K, int H, float scale, void* out, int out_dt,
                           hipStream_t s) {
-  if (T <= 0) return hipSuccess;
+  if (T <= 0 || H <= 0) return hipSuccess;
   const bool vec = (H % 8) == 0;
-#define MOE_COMBINE(D)                                                                   \
-  (vec ? combine_kernel<D, true><<<T, 256, 0, s>>>(y, w, route_pos, T, K, H, scale, out, out_dt) \
-       : combine_kernel<D, false><<<T, 256, 0, s>>>(y, w, route_pos, T, K, H, scale, out, out_dt))
+  const dim3 grid(T, (H + kChunk - 1) / kChunk);
+#define MOE_COMBINE(D)                                                                        \
+  (vec ? combine_kernel<D, true><<<grid, kThreads, 0, s>>>(y, w, route_pos, T, K, H, scale, out, \
+                                                           out_dt)                             \
+       : combine_kernel<D, false><<<grid, kThreads, 0, s>>>(y, w, route_pos, T, K, H, scale, out, \
+                                                            out_dt))
   if (y_dt == 0) MOE_COMBINE(0);
   else if (y_dt == 1) MOE_COMBINE(1);
   else MOE_COMBINE(2);
