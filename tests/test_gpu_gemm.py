@@ -105,3 +105,51 @@ def test_gemm_large_expert_rows():
     torch.cuda.synchronize()
     ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(), None, "bf16")
     assert_close(np64(out), ref, "bf16", "large M")
+
+
+# More tiles than workgroups (one per CU), so each workgroup walks several tiles and the
+# LDS ring runs across tile boundaries, expert changes and ragged contractions:
+# rows 3000 + 0 + 2500 + 1 + 4000 give 77 row tiles (308-462 tiles with these widths).
+MANY_TILES = [3000, 0, 2500, 1, 4000]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+@pytest.mark.parametrize("Kd,N", [(200, 1000), (64, 1000), (40, 1300), (1096, 776)])
+def test_gemm_many_tiles_per_workgroup(dt, Kd, N):
+    sizes = MANY_TILES
+    E, M = len(sizes), int(sum(sizes))
+    say(f"[gemm-many] dt={dt} K={Kd} N={N}")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn((M, Kd), device="cuda", generator=g).to(DT[dt])
+    b = (0.1 * torch.randn((E, N, Kd), device="cuda", generator=g)).to(DT[dt])
+    bb = (0.1 * torch.randn((E, N), device="cuda", generator=g)).to(DT[dt])
+    off = _offsets(sizes)
+    out, check = guarded((M, N), DT[dt])
+    B.moe_grouped_gemm(a, b, off, bb, out=out)
+    torch.cuda.synchronize()
+    check()
+    ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(), np64(bb), dt)
+    assert_close(np64(out), ref, dt, f"many tiles K={Kd}")
+
+
+@pytest.mark.parametrize("act", ["silu_and_mul", "swigluoai", "gelu_and_mul"])
+@pytest.mark.parametrize("H", [136, 64, 1096])
+def test_gemm_act_many_tiles_per_workgroup(act, H):
+    """Gated activation and gathered rows over more tiles than workgroups (F 520: five
+    activation tiles per row tile, the last ragged)."""
+    sizes = MANY_TILES
+    E, M, F = len(sizes), int(sum(sizes)), 520
+    say(f"[gemm-act-many] act={act} H={H}")
+    g = torch.Generator(device="cuda").manual_seed(4)
+    T = M // 4 + 1
+    src = (2.0 * torch.randn((T, H), device="cuda", generator=g)).to(torch.bfloat16)
+    w = (0.1 * torch.randn((E, 2 * F, H), device="cuda", generator=g)).to(torch.bfloat16)
+    rows = torch.randint(0, 4 * T, (M,), device="cuda", generator=g).to(torch.int32)
+    off = _offsets(sizes)
+    out, check = guarded((M, F), torch.bfloat16)
+    B.moe_grouped_gemm_swiglu(src, w, off, act, None, a_rows=rows, a_rows_div=4, M=M, out=out)
+    torch.cuda.synchronize()
+    check()
+    a_np = np64(src)[rows.cpu().numpy() // 4]
+    ref = O.grouped_gemm_act(a_np, np64(w), off.cpu().numpy(), act, None, "bf16")
+    assert_close(np64(out), ref, "bf16", f"act many tiles {act} H={H}")
