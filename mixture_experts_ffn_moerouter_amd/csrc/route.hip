@@ -34,43 +34,89 @@ __device__ __forceinline__ int key_index(uint64_t k) {
   return (int)(0xffffffffu - (uint32_t)(k & 0xffffffffu));
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
+// Wave reductions (every lane of the wave active). Inside each 16-lane row, four DPP
+// exchanges (swap neighbours, swap pairs, mirror halves of 8, mirror the row) leave every
+// lane with its row's result; the four rows are then combined from lanes 0, 16, 32, 48 in
+// scalar registers, so the result is wave-uniform. No LDS-crossbar shuffles.
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141;  // row_half_mirror
+constexpr int kDppMirror = 0x140;      // row_mirror
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __uint_as_float(lane_u32(__float_as_uint(v), l));
+}
+__device__ __forceinline__ int lane_i32(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int l) {
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), l) << 32) | lane_u32((uint32_t)v, l);
 }
 
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = max_u64(v, dpp_u64<kDppSwap1>(v));
+  v = max_u64(v, dpp_u64<kDppSwap2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  v = max_u64(v, dpp_u64<kDppMirror>(v));
+  return max_u64(max_u64(lane_u64(v, 0), lane_u64(v, 16)),
+                 max_u64(lane_u64(v, 32), lane_u64(v, 48)));
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 
+// Sum in a fixed tree order (deterministic for a given wave content).
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_f32<kDppSwap1>(v);
+  v += dpp_f32<kDppSwap2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 
-// Top two values of a wave (a1 >= a2 in every lane on entry and exit).
+// Top two of (a1, a2) and (b1, b2), each pair ordered: the largest and the second largest
+// of the four values (duplicates count separately).
+__device__ __forceinline__ void top2_merge(float& a1, float& a2, float b1, float b2) {
+  const float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
+  a1 = fmaxf(a1, b1);
+  a2 = n2;
+}
+template <int CTRL>
+__device__ __forceinline__ void top2_step(float& a1, float& a2) {
+  top2_merge(a1, a2, dpp_f32<CTRL>(a1), dpp_f32<CTRL>(a2));
+}
+
+// Top two values of a wave (a1 >= a2 in every lane on entry; uniform on exit).
 __device__ __forceinline__ void wave_top2(float& a1, float& a2) {
+  top2_step<kDppSwap1>(a1, a2);
+  top2_step<kDppSwap2>(a1, a2);
+  top2_step<kDppHalfMirror>(a1, a2);
+  top2_step<kDppMirror>(a1, a2);
+  float r1 = lane_f32(a1, 0), r2 = lane_f32(a2, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    float b1 = __shfl_xor(a1, m, 64), b2 = __shfl_xor(a2, m, 64);
-    float n1 = fmaxf(a1, b1);
-    float n2 = fmaxf(fminf(a1, b1), fmaxf(a2, b2));
-    a1 = n1;
-    a2 = n2;
-  }
+  for (int l = 16; l < 64; l += 16) top2_merge(r1, r2, lane_f32(a1, l), lane_f32(a2, l));
+  a1 = r1;
+  a2 = r2;
 }
 
 template <int PL>
@@ -127,13 +173,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
   if (p.expert_ids) {
     // ---- hash routing: the given experts, bias and groups ignored
     for (int k = 0; k < K; ++k) {
-      int e = p.expert_ids[(int64_t)t * K + k];
-      int slot = e >> 6;
+      const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[(int64_t)t * K + k]);
+      const int slot = e >> 6;
       float v = 0.f;
 #pragma unroll
       for (int j = 0; j < PL; ++j)
         if (j == slot) v = s[j];
-      float w = __shfl(v, e & 63, 64);
+      const float w = lane_f32(v, e & 63);
       wsum += w;
       if (lane == k) { my_sel = e; my_w = w; }
     }
@@ -184,9 +230,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
 #pragma unroll
       for (int j = 0; j < PL; ++j)
         if (keys[j] > best) { best = keys[j]; best_s = s[j]; }
-      uint64_t m = wave_max_u64(best);
-      int e = key_index(m);
-      float w = __shfl(best_s, e & 63, 64);
+      const uint64_t m = wave_max_u64(best);
+      const int e = key_index(m);
+      const float w = lane_f32(best_s, e & 63);
 #pragma unroll
       for (int j = 0; j < PL; ++j)
         if (lane + 64 * j == e) keys[j] = 0ull;
@@ -208,16 +254,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
     const float fill = p.rp_dtype == 2 ? -1.0e4f : -1.0e30f;
     float w_local = 0.f;  // k ascending, uniform
     for (int k = 0; k < K; ++k) {
-      int e = __shfl(my_sel, k, 64);
-      float w = __shfl(wn, k, 64);
+      const int e = lane_i32(my_sel, k);
+      const float w = lane_f32(wn, k);
       if (e >= a0 && e < a0 + n) w_local += w;
     }
     for (int c0 = 0; c0 < n; c0 += 64) {
       int c = c0 + lane;
       float v = fill;
       for (int k = 0; k < K; ++k) {
-        int e = __shfl(my_sel, k, 64);
-        float w = __shfl(wn, k, 64);
+        const int e = lane_i32(my_sel, k);
+        const float w = lane_f32(wn, k);
         if (e == a0 + c) v = logf(w);
       }
       if (c < n) store_dt(p.router_probs, p.rp_dtype, (int64_t)t * n + c, v);
