@@ -89,7 +89,8 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
     const int e = e0 + tid;
     int tot = 0, before = 0;
     if (e < E)
-      for (int bb = 0; bb < nblk; ++bb) {
+#pragma unroll 8
+      for (int bb = 0; bb < nblk; ++bb) {  // unrolled: the count loads go out together
         const int c = blk_cnt[(int64_t)bb * E + e];
         tot += c;
         before += bb < b ? c : 0;
