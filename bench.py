@@ -42,11 +42,11 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # was measured on: gemm_src is the SHA-256 of that kernel's file and csrc/tile_map.h at the
 # time, and a different source reports null.
 TRAFFIC = {
-    # FETCH_SIZE KiB x 1.99994 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
-    # 524302.6 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE).
-    # gate_up: 503987.9 + 50469.9 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1083819655,
-                   "gemm_src": "394f70830efa4c3a8f31f2e49131b56c2fb5ac9a0b0030b120bdece6fc3e317a"},
+    # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
+    # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE).
+    # gate_up: 500898.3 + 50120.7 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1077137488,
+                   "gemm_src": "7cf169e11cc66834da1d9f851ef669ed1f1512760774557ff5b25c9674364282"},
     # FP8 (a 1 GiB copy read 524301.2 KiB of FETCH_SIZE): 4512238.0 + 263745.7 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9510906364,
                          "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},

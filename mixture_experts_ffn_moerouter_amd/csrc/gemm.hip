@@ -45,6 +45,7 @@
 // expert, n-tile, row tile and each XCD takes a contiguous range, its workgroups
 // striding through it together: the row tiles that share a weight slice run side by side
 // on one L2, and so do the n-tiles sharing the expert's token rows.
+#include <atomic>
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -430,18 +431,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g) {
 }
 
 
+// Compute units of the current device (cached per device; 256 if the query fails). The
+// persistent grid is sized by it; results do not depend on it.
 int cu_count() {
-  static int n = 0;  // per process; every device used here has the same count
-  if (n == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        v > 0)
-      n = v;
-    else
-      n = 256;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
   }
-  return n;
+  int v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      v <= 0)
+    v = 256;
+  if (dev < kMaxDevices) cached[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT>
