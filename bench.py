@@ -522,7 +522,7 @@ def cpu_baseline(cfg, d, budget_s: float):
                       f"float64 numpy oracle, {total:.1f} s wall"}
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -537,7 +537,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--host-inputs", action="store_true",
                     help="FP8 workloads: replicate one host-generated expert (counter runs)")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the path is built and measured on a single "
               "MI355X (no collectives); use --gpus 1.", file=sys.stderr)
