@@ -166,7 +166,8 @@ int moe_abi_version(void);
  * weight_scale    [T] in router_probs_dtype, or NULL (given together with
  *                 router_probs): routed_scaling_factor * sum of the normalized weights
  *                 of the chosen experts in the slice; exactly 0 with none [MR].
- * Errors: INVALID_ARG for null logits/topk outputs, E < 1, E > 512, bad cfg fields;
+ * Errors: INVALID_ARG for null logits/topk outputs, E < 1, bad cfg fields;
+ * UNSUPPORTED for E > 512 or T * max(E, top_k) >= 2^31;
  * OVERLAP if an output overlaps logits/bias/expert_ids or another output.
  * ------------------------------------------------------------------------------- */
 int moe_route(const void* logits, int64_t T, int64_t E, const float* correction_bias,
