@@ -52,6 +52,13 @@ SMALL = {
                                       correction_bias=(-0.1, 0.1), logits_dtype="bf16"),
     "f16_logits_softmax": I.MoEConfig("f16_logits_softmax", T=300, H=256, E=16, F=192, K=4,
                                       logits_dtype="f16"),
+    # E at the router's maximum of 512, through each backend
+    "max_experts_staged": I.MoEConfig("max_experts_staged", T=400, H=128, E=512, F=64, K=8,
+                                      scoring="sigmoid", G=8, TG=4,
+                                      correction_bias=(-0.1, 0.1), rsf=2.5),
+    "decode_max_experts": I.MoEConfig("decode_max_experts", T=64, H=128, E=512, F=256, K=8,
+                                      scoring="sigmoid", G=8, TG=4,
+                                      correction_bias=(-0.1, 0.1), rsf=2.5),
 }
 
 

@@ -153,3 +153,51 @@ def test_gemm_act_many_tiles_per_workgroup(act, H):
     a_np = np64(src)[rows.cpu().numpy() // 4]
     ref = O.grouped_gemm_act(a_np, np64(w), off.cpu().numpy(), act, None, "bf16")
     assert_close(np64(out), ref, "bf16", f"act many tiles {act} H={H}")
+
+
+def _max_expert_sizes(seed):
+    """1024 experts (the documented maximum): about a third empty, the rest 1..40 rows."""
+    rng = np.random.default_rng(seed)
+    sizes = rng.integers(1, 41, size=1024)
+    sizes[rng.random(1024) < 0.33] = 0
+    return sizes
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_gemm_max_experts(dt):
+    """E at its maximum of 1024: the tile map of every expert fits in LDS."""
+    sizes = _max_expert_sizes(5)
+    E, M, Kd, N = len(sizes), int(sizes.sum()), 136, 72
+    say(f"[gemm-maxE] dt={dt} E={E} M={M}")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    a = torch.randn((M, Kd), device="cuda", generator=g).to(DT[dt])
+    b = (0.1 * torch.randn((E, N, Kd), device="cuda", generator=g)).to(DT[dt])
+    bb = (0.1 * torch.randn((E, N), device="cuda", generator=g)).to(DT[dt])
+    off = _offsets(sizes)
+    out, check = guarded((M, N), DT[dt])
+    B.moe_grouped_gemm(a, b, off, bb, out=out)
+    torch.cuda.synchronize()
+    check()
+    ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(), np64(bb), dt)
+    assert_close(np64(out), ref, dt, "gemm E=1024")
+
+
+def test_gemm_act_max_experts():
+    """Gated activation with gathered rows over 1024 experts."""
+    sizes = _max_expert_sizes(6)
+    E, M, H, F = len(sizes), int(sizes.sum()), 136, 48
+    say(f"[gemm-act-maxE] E={E} M={M}")
+    g = torch.Generator(device="cuda").manual_seed(6)
+    T = M // 8 + 1
+    src = (2.0 * torch.randn((T, H), device="cuda", generator=g)).to(torch.bfloat16)
+    w = (0.1 * torch.randn((E, 2 * F, H), device="cuda", generator=g)).to(torch.bfloat16)
+    rows = torch.randint(0, 8 * T, (M,), device="cuda", generator=g).to(torch.int32)
+    off = _offsets(sizes)
+    out, check = guarded((M, F), torch.bfloat16)
+    B.moe_grouped_gemm_swiglu(src, w, off, "silu_and_mul", None, a_rows=rows, a_rows_div=8,
+                              M=M, out=out)
+    torch.cuda.synchronize()
+    check()
+    a_np = np64(src)[rows.cpu().numpy() // 8]
+    ref = O.grouped_gemm_act(a_np, np64(w), off.cpu().numpy(), "silu_and_mul", None, "bf16")
+    assert_close(np64(out), ref, "bf16", "act E=1024")

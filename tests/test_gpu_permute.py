@@ -24,7 +24,7 @@ def _ids(T, K, E, skew=False, seed=0):
 @pytest.mark.parametrize("T,K,E,skew", [(1, 1, 1, False), (7, 3, 5, False),
                                         (333, 4, 16, False), (4096, 8, 128, False),
                                         (4096, 8, 256, False), (2048, 4, 128, False),
-                                        (16, 8, 256, False), (1000, 5, 1000, False),
+                                        (16, 8, 256, False), (1000, 5, 1000, False), (2000, 8, 1024, False),
                                         (500, 4, 64, True), (16384, 8, 256, False)])
 def test_permute_bit_exact(T, K, E, skew):
     say(f"[permute] T={T} K={K} E={E} skew={skew}")
