@@ -1,5 +1,6 @@
-// Router kernel: scoring, (grouped) top-k selection, weights and the expert-parallel
-// router row, one wave64 per token.
+// Router kernels: scoring, (grouped) top-k selection, weights and the expert-parallel
+// router row; one wave64 per token, or four tokens per wave (one per 16-lane row) for
+// batches of 1024 tokens or more in the common configurations.
 //
 // [MR] ONNX Runtime PR 32126 "[CUDA] Add MoERouter and SwiGLU contrib operators",
 //      MoERouter: scoring softmax | sigmoid | sqrt_softplus, selection topk | noaux_tc
@@ -272,9 +273,261 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
   }
 }
 
+
+// ---------------------------------------------------------------------------------
+// Row router: four tokens per wave, one per 16-lane row. Lane l of a row holds experts
+// l, l + 16, l + 32, ... (EPL of them). Every reduction is the four in-row DPP steps, so a
+// row's result reaches all of its lanes without leaving the row, and four tokens share
+// each instruction. It covers the common configurations: no expert_ids, top_k <= 16,
+// and either no groups or G = EPL / M groups of 16 M experts (E = 16 EPL), G <= 16. The
+// selections are those of route_kernel (same keys, same k order for the weight sum);
+// only the softmax denominator is summed in another order.
+constexpr int kRowLanes = 16;
+constexpr int kRowTokens = 4;  // tokens per wave
+
+template <int CTRL>
+__device__ __forceinline__ void key_score_step(uint64_t& k, float& s) {
+  const uint64_t ok = dpp_u64<CTRL>(k);
+  const float os = dpp_f32<CTRL>(s);
+  if (ok > k) {
+    k = ok;
+    s = os;
+  }
+}
+
+// Largest key of the row and the score carried with it, in every lane of the row.
+__device__ __forceinline__ void row_max_key_score(uint64_t& k, float& s) {
+  key_score_step<kDppSwap1>(k, s);
+  key_score_step<kDppSwap2>(k, s);
+  key_score_step<kDppHalfMirror>(k, s);
+  key_score_step<kDppMirror>(k, s);
+}
+
+__device__ __forceinline__ uint64_t row_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<kDppSwap1>(v));
+  v = max_u64(v, dpp_u64<kDppSwap2>(v));
+  v = max_u64(v, dpp_u64<kDppHalfMirror>(v));
+  return max_u64(v, dpp_u64<kDppMirror>(v));
+}
+
+__device__ __forceinline__ float row_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f32<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f32<kDppMirror>(v));
+}
+
+// Same value in every lane of the row: each step adds two equal partial sums in either
+// order, and float addition is commutative.
+__device__ __forceinline__ float row_sum_f32(float v) {
+  v += dpp_f32<kDppSwap1>(v);
+  v += dpp_f32<kDppSwap2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  return v + dpp_f32<kDppMirror>(v);
+}
+
+__device__ __forceinline__ void row_top2(float& a1, float& a2) {
+  top2_step<kDppSwap1>(a1, a2);
+  top2_step<kDppSwap2>(a1, a2);
+  top2_step<kDppHalfMirror>(a1, a2);
+  top2_step<kDppMirror>(a1, a2);
+}
+
+// Value of lane src (0..63) of the wave, for every lane.
+__device__ __forceinline__ int lane_fetch(int v, int src) {
+  return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
+
+// EPL experts per lane; M > 0: groups of 16 M experts (M per lane), G = EPL / M.
+template <int EPL, int M>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void route_rows_kernel(RouteArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int l = lane & (kRowLanes - 1), row0 = lane & ~(kRowLanes - 1);
+  const int t0 = (blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6)) * kRowTokens;
+  if (t0 >= p.T) return;  // uniform per wave
+  const int t = t0 + (lane >> 4);
+  const bool live = t < p.T;  // rows past the last token compute on nothing
+  const int E = p.E;
+  const int64_t z0 = (int64_t)t * E;
+
+  float s[EPL], u[EPL];
+  bool valid[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = l + kRowLanes * j;
+    valid[j] = live && e < E;
+    s[j] = valid[j] ? load_dt(p.logits, p.logits_dt, z0 + e) : -INFINITY;
+  }
+  // ---- scoring, float32
+  if (p.scoring == 0) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) m = fmaxf(m, s[j]);
+    m = row_max_f32(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      s[j] = valid[j] ? expf(s[j] - m) : 0.f;
+      sum += s[j];
+    }
+    sum = row_sum_f32(sum);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s[j] = s[j] / sum;
+  } else if (p.scoring == 1) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) s[j] = valid[j] ? 1.0f / (1.0f + expf(-s[j])) : 0.f;
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      s[j] = valid[j] ? sqrtf(fmaxf(s[j], 0.f) + log1pf(expf(-fabsf(s[j])))) : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = l + kRowLanes * j;
+    u[j] = (p.bias && valid[j]) ? s[j] + p.bias[e] : s[j];
+  }
+
+  bool elig[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) elig[j] = valid[j];
+  if constexpr (M > 0) {
+    // ---- group limit: group g = experts [16 M g, 16 M (g + 1)), slots j in [M g, M (g+1))
+    constexpr int G = EPL / M;
+    float my_gs = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float a1 = -INFINITY, a2 = -INFINITY;
+#pragma unroll
+      for (int j = g * M; j < (g + 1) * M; ++j)
+        if (valid[j]) {
+          const float v = u[j];
+          if (v > a1) {
+            a2 = a1;
+            a1 = v;
+          } else if (v > a2) {
+            a2 = v;
+          }
+        }
+      row_top2(a1, a2);
+      if (l == g) my_gs = p.bias ? a1 + a2 : a1;  // a group holds 16 M >= 2 experts
+    }
+    uint64_t gkey = l < G ? make_key(my_gs, l) : 0ull;
+    uint32_t kept = 0;
+    for (int i = 0; i < p.TG; ++i) {
+      const int g = key_index(row_max_u64(gkey));
+      kept |= 1u << g;
+      if (l == g) gkey = 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) elig[j] = valid[j] && ((kept >> (j / M)) & 1u);
+  }
+
+  // ---- top-k: K rounds of a row-wide max; lane k of the row keeps the k-th pick
+  uint64_t keys[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) keys[j] = elig[j] ? make_key(u[j], l + kRowLanes * j) : 0ull;
+  const int K = p.K;
+  int my_sel = 0;
+  float my_w = 0.f, wsum = 0.f;
+  for (int k = 0; k < K; ++k) {
+    uint64_t best = 0ull;
+    float best_s = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (keys[j] > best) {
+        best = keys[j];
+        best_s = s[j];
+      }
+    row_max_key_score(best, best_s);
+    const int e = key_index(best);
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (l + kRowLanes * j == e) keys[j] = 0ull;
+    wsum += best_s;
+    if (l == k) {
+      my_sel = e;
+      my_w = best_s;
+    }
+  }
+
+  const float wn = p.renormalize ? my_w / wsum : my_w;
+  if (live && l < K) {
+    p.topk_w[(int64_t)t * K + l] = wn * p.rsf;
+    p.topk_ids[(int64_t)t * K + l] = my_sel;
+  }
+
+  // ---- expert-parallel router row and scale
+  if (p.router_probs) {
+    const int a0 = p.local_start, n = p.local_count;
+    const float fill = p.rp_dtype == 2 ? -1.0e4f : -1.0e30f;
+    float w_local = 0.f;  // k ascending
+    for (int k = 0; k < K; ++k) {
+      const int e = lane_fetch(my_sel, row0 + k);
+      const float w = __int_as_float(lane_fetch(__float_as_int(wn), row0 + k));
+      if (e >= a0 && e < a0 + n) w_local += w;
+    }
+    for (int c0 = 0; c0 < n; c0 += kRowLanes) {
+      const int c = c0 + l;
+      float v = fill;
+      for (int k = 0; k < K; ++k) {
+        const int e = lane_fetch(my_sel, row0 + k);
+        const float w = __int_as_float(lane_fetch(__float_as_int(wn), row0 + k));
+        if (e == a0 + c) v = logf(w);
+      }
+      if (live && c < n) store_dt(p.router_probs, p.rp_dtype, (int64_t)t * n + c, v);
+    }
+    if (live && l == 0) store_dt(p.weight_scale, p.rp_dtype, t, p.rsf * w_local);
+  }
+}
+
+template <int EPL>
+void launch_rows(const RouteArgs& a, int m, dim3 grid, dim3 block, hipStream_t s) {
+  if (m == 0) route_rows_kernel<EPL, 0><<<grid, block, 0, s>>>(a);
+  else if constexpr (EPL >= 8) {
+    if (m == 1) route_rows_kernel<EPL, 1><<<grid, block, 0, s>>>(a);
+    else if (m == 2) route_rows_kernel<EPL, 2><<<grid, block, 0, s>>>(a);
+    else route_rows_kernel<EPL, 4><<<grid, block, 0, s>>>(a);
+  }
+}
+
+// Experts per lane of the row router for this configuration, or 0 when it does not apply.
+// *m: experts per lane in one group (0 without groups).
+// Below kRowsMinTokens the one-token-per-wave kernel is faster: with fewer waves than
+// SIMDs, a token's serial latency decides the time, and a row lane holds 4x the experts.
+constexpr int kRowsMinTokens = 1024;
+
+int rows_epl(const RouteArgs& a, int* m) {
+  *m = 0;
+  if (a.T < kRowsMinTokens || a.expert_ids || a.K > kRowLanes || a.E > 512) return 0;
+  const int epl = a.E <= 16 ? 1 : a.E <= 32 ? 2 : a.E <= 64 ? 4 : a.E <= 128 ? 8
+                : a.E <= 256 ? 16 : 32;
+  if (a.G <= 1) return epl;
+  const int gsz = a.E / a.G;
+  if (a.E != kRowLanes * epl || epl < 8 || gsz % kRowLanes) return 0;
+  const int mm = gsz / kRowLanes;
+  if ((mm != 1 && mm != 2 && mm != 4) || epl / mm > kRowLanes) return 0;
+  *m = mm;
+  return epl;
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  int m = 0;
+  const int epl = rows_epl(a, &m);
+  if (epl > 0) {
+    const int per_block = kWavesPerBlock * kRowTokens;
+    const dim3 grid((a.T + per_block - 1) / per_block), block(64 * kWavesPerBlock);
+    switch (epl) {
+      case 1: launch_rows<1>(a, m, grid, block, s); break;
+      case 2: launch_rows<2>(a, m, grid, block, s); break;
+      case 4: launch_rows<4>(a, m, grid, block, s); break;
+      case 8: launch_rows<8>(a, m, grid, block, s); break;
+      case 16: launch_rows<16>(a, m, grid, block, s); break;
+      default: launch_rows<32>(a, m, grid, block, s); break;
+    }
+    return hipGetLastError();
+  }
   dim3 grid((a.T + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
   if (a.E <= 64) route_kernel<1><<<grid, block, 0, s>>>(a);
   else if (a.E <= 128) route_kernel<2><<<grid, block, 0, s>>>(a);

@@ -25,6 +25,18 @@ ROUTE_CASES = {
     "K_equals_E": (50, 8, 8, "softmax", False, 1.0, 1, 1, False, False),
     "hash_routing": (333, 96, 5, "sigmoid", True, 1.5, 4, 2, True, True),
     "E1": (40, 1, 1, "sigmoid", True, 1.0, 1, 1, False, False),
+    # 1024 tokens or more: the four-tokens-per-wave kernel (T % 16 != 0 leaves idle rows)
+    "rows_sqrt_softplus": (1030, 256, 8, "sqrt_softplus", True, 1.0, 1, 1, False, False),
+    "rows_E512_groups": (1500, 512, 16, "sigmoid", True, 2.827, 16, 6, True, False),
+    "rows_E40": (1111, 40, 6, "softmax", True, 1.0, 1, 1, False, False),
+    "rows_E8_K_equals_E": (1024, 8, 8, "softmax", False, 1.0, 1, 1, False, False),
+    "rows_groups_of_16": (1200, 128, 4, "sigmoid", True, 1.0, 8, 3, True, False),
+    "rows_groups_of_64": (1100, 256, 8, "sigmoid", False, 1.0, 4, 2, True, False),
+    "rows_K16": (1050, 64, 16, "softmax", True, 1.0, 1, 1, False, False),
+    # large batches the row kernel does not take: top_k 17, groups of 8, hash routing
+    "large_K17": (1030, 64, 17, "sigmoid", True, 1.0, 1, 1, False, False),
+    "large_groups_of_8": (1100, 64, 4, "softmax", False, 1.0, 8, 3, False, False),
+    "large_hash_routing": (1040, 96, 5, "sigmoid", True, 1.5, 4, 2, True, True),
 }
 
 
@@ -51,10 +63,11 @@ def test_route_parity(name):
 
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("slice_", [(64, 64), (0, 256), (250, 6)])
-def test_router_ep_outputs(dt, slice_):
+@pytest.mark.parametrize("T", [256, 1030])
+def test_router_ep_outputs(dt, slice_, T):
     start, count = slice_
-    T, E, K = 256, 256, 8
-    say(f"[route-ep] dt={dt} slice={slice_}")
+    E, K = 256, 8
+    say(f"[route-ep] dt={dt} slice={slice_} T={T}")
     logits = I.normal((T, E), 1.0, seed=3, stream=1, device="cuda")
     cfg = B.route_cfg(K, "sqrt_softplus", True, 1.25, local_expert_start=start,
                       local_expert_count=count, router_probs_dtype=dt)
@@ -124,11 +137,12 @@ def test_route_deterministic():
 @pytest.mark.parametrize("ldt", ["bf16", "f16"])
 @pytest.mark.parametrize("scoring,groups", [("softmax", (1, 1)), ("sigmoid", (8, 4)),
                                             ("sqrt_softplus", (1, 1))])
-def test_route_16bit_logits(ldt, scoring, groups):
+@pytest.mark.parametrize("T", [1000, 1030])
+def test_route_16bit_logits(ldt, scoring, groups, T):
     """bfloat16 / float16 logits ([TO] FusedTopKFwdOp): each value is read exactly into
     float32, so the result is the oracle's on the same (exactly widened) values."""
     G, TG = groups
-    T, E, K = 1000, 256, 8
+    E, K = 256, 8
     say(f"[route] {ldt} logits, {scoring}, groups {groups}")
     g = torch.Generator(device="cuda").manual_seed(5)
     logits = (2.0 * torch.randn((T, E), device="cuda", generator=g)).to(
