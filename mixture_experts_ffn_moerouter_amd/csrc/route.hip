@@ -120,6 +120,47 @@ __device__ __forceinline__ void wave_top2(float& a1, float& a2) {
   a2 = r2;
 }
 
+// The N logits of a lane (experts first + STRIDE j of row z0), widened to float32, -inf
+// where not valid. The dtype is dispatched once outside the loop, so the N loads are
+// issued back to back instead of each behind its own branch.
+template <int N, int STRIDE>
+__device__ __forceinline__ void load_logits(const RouteArgs& p, int64_t z0, int first,
+                                            const bool* valid, float* s) {
+  if (p.logits_dt == 0) {
+    const float* x = (const float*)p.logits + z0 + first;
+#pragma unroll
+    for (int j = 0; j < N; ++j) s[j] = valid[j] ? x[STRIDE * j] : -INFINITY;
+  } else {
+    const uint16_t* x = (const uint16_t*)p.logits + z0 + first;
+    uint16_t h[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) h[j] = valid[j] ? x[STRIDE * j] : (uint16_t)0;
+    if (p.logits_dt == 1) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) s[j] = valid[j] ? bf16_to_f32(h[j]) : -INFINITY;
+    } else {
+#pragma unroll
+      for (int j = 0; j < N; ++j) s[j] = valid[j] ? f16_to_f32(h[j]) : -INFINITY;
+    }
+  }
+}
+
+// u = s + bias (noaux_tc) where a bias is given and the expert is valid, else s.
+template <int N, int STRIDE>
+__device__ __forceinline__ void add_bias(const RouteArgs& p, int first, const bool* valid,
+                                         const float* s, float* u) {
+  if (p.bias) {
+    float b[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) b[j] = valid[j] ? p.bias[first + STRIDE * j] : 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j) u[j] = valid[j] ? s[j] + b[j] : s[j];
+  } else {
+#pragma unroll
+    for (int j = 0; j < N; ++j) u[j] = s[j];
+  }
+}
+
 template <int PL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p) {
   const int lane = threadIdx.x & 63;
@@ -131,11 +172,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
   float s[PL], u[PL];
   bool valid[PL];
 #pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    int e = lane + 64 * j;
-    valid[j] = e < E;
-    s[j] = valid[j] ? load_dt(p.logits, p.logits_dt, z0 + e) : -INFINITY;
-  }
+  for (int j = 0; j < PL; ++j) valid[j] = lane + 64 * j < E;
+  load_logits<PL, 64>(p, z0, lane, valid, s);
   // ---- scoring, float32
   if (p.scoring == 0) {  // softmax over all E experts
     float m = -INFINITY;
@@ -159,11 +197,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(RouteArgs p)
     for (int j = 0; j < PL; ++j)
       s[j] = valid[j] ? sqrtf(fmaxf(s[j], 0.f) + log1pf(expf(-fabsf(s[j])))) : 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    int e = lane + 64 * j;
-    u[j] = (p.bias && valid[j]) ? s[j] + p.bias[e] : s[j];
-  }
+  add_bias<PL, 64>(p, lane, valid, s, u);
 
   // Lane k (< K) ends up holding the k-th chosen expert and its unbiased score.
   int my_sel = 0;
@@ -353,11 +387,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_rows_kernel(RouteAr
   float s[EPL], u[EPL];
   bool valid[EPL];
 #pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = l + kRowLanes * j;
-    valid[j] = live && e < E;
-    s[j] = valid[j] ? load_dt(p.logits, p.logits_dt, z0 + e) : -INFINITY;
-  }
+  for (int j = 0; j < EPL; ++j) valid[j] = live && l + kRowLanes * j < E;
+  load_logits<EPL, kRowLanes>(p, z0, l, valid, s);
   // ---- scoring, float32
   if (p.scoring == 0) {
     float m = -INFINITY;
@@ -381,11 +412,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_rows_kernel(RouteAr
     for (int j = 0; j < EPL; ++j)
       s[j] = valid[j] ? sqrtf(fmaxf(s[j], 0.f) + log1pf(expf(-fabsf(s[j])))) : 0.f;
   }
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = l + kRowLanes * j;
-    u[j] = (p.bias && valid[j]) ? s[j] + p.bias[e] : s[j];
-  }
+  add_bias<EPL, kRowLanes>(p, l, valid, s, u);
 
   bool elig[EPL];
 #pragma unroll
