@@ -12,6 +12,7 @@ launch by launch with HIP events on the stream it runs on, inside complete layer
 through the separate entry points.
 """
 import argparse
+import ctypes
 import dataclasses
 import hashlib
 import json
@@ -145,6 +146,21 @@ def time_launches(call, reps: int, stream) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
+def time_burst(call, reps: int, stream) -> float:
+    """Average duration in ms of one call over back-to-back launches, HIP events around the
+    whole burst on the stream the kernels run on (for calls shorter than their host-side
+    launch cost, where events around each launch would time the host)."""
+    for _ in range(3):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        call()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def time_gate_up(cfg, d, reps: int):
     """Average duration of the grouped gate_up GEMM launch, timed inside complete layers.
 
@@ -197,8 +213,19 @@ def router_line(cfg, args):
                        cfg.router_probs_dtype or "f32")
     stream = torch.cuda.current_stream()
     ep = cfg.local_expert_count is not None
-    call = lambda: B.moe_route(d["logits"], rcfg, d.get("correction_bias"),
-                               d.get("expert_ids"), with_router_probs=ep, stream=stream)
+    # One routing call is a few microseconds of GPU work, less than the Python binding
+    # spends marshalling a call. The timed calls therefore go to the C ABI the way a
+    # native caller makes them: outputs allocated and arguments marshalled once.
+    w, ids, rp, ws = B.moe_route(d["logits"], rcfg, d.get("correction_bias"),
+                                 d.get("expert_ids"), with_router_probs=ep, stream=stream)
+    c = B.MoeRouteCfg.from_buffer_copy(rcfg)
+    c.logits_dtype = B.TORCH_DTYPES[d["logits"].dtype]
+    raw = (B._ptr(d["logits"]), cfg.T, cfg.E, B._ptr(d.get("correction_bias")),
+           B._ptr(d.get("expert_ids")), ctypes.byref(c), B._ptr(w), B._ptr(ids), B._ptr(rp),
+           B._ptr(ws), B._stream(stream))
+    lib = B.lib()
+    B._check("moe_route", lib.moe_route(*raw))
+    call = lambda: lib.moe_route(*raw)
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -207,7 +234,7 @@ def router_line(cfg, args):
         call()
     torch.cuda.synchronize()
     ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    k_ms = time_launches(call, args.kernel_reps, stream)
+    k_ms = time_burst(call, args.kernel_reps, stream)
     rp = 2 if cfg.router_probs_dtype in ("f16", "bf16") else 4
     lg = 2 if cfg.logits_dtype in ("f16", "bf16") else 4
     k_bytes = cfg.T * cfg.E * lg + (cfg.E * 4 if cfg.correction_bias else 0) \
@@ -228,7 +255,8 @@ def router_line(cfg, args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 6),
                      "traffic": None,
-                     "kernel": "route_kernel" + (" (launch-bound: tiny input)" if cfg.T <= 64 else ""),
+                     "kernel": "router kernel of moe_route" + (" (launch-bound: tiny input)"
+                                                                 if cfg.T <= 64 else ""),
                      "kernel_ms": round(k_ms, 5), "latency_us": round(k_ms * 1e3, 2),
                      "algorithmic_bytes": k_bytes},
     }
