@@ -234,7 +234,7 @@ int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows
  * out             [M, N] in out_dt (dt or MOE_F32). Rows outside every expert are left
  *                 unwritten.
  * Limits: K % 8 == 0 for bf16/f16, E <= 1024, M*K*2 and N*K*2 below 2^31 bytes for
- * bf16/f16.
+ * bf16/f16 (32-bit offsets; a gathered source must also stay below 2^31 bytes).
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP.
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm(const void* a, const int32_t* a_rows, int32_t a_rows_div, int64_t M,
