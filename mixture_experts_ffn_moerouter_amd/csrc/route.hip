@@ -507,14 +507,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_rows_kernel(RouteAr
   }
 }
 
+// false if this (EPL, m) has no instance (nothing launched).
 template <int EPL>
-void launch_rows(const RouteArgs& a, int m, dim3 grid, dim3 block, hipStream_t s) {
-  if (m == 0) route_rows_kernel<EPL, 0><<<grid, block, 0, s>>>(a);
-  else if constexpr (EPL >= 8) {
-    if (m == 1) route_rows_kernel<EPL, 1><<<grid, block, 0, s>>>(a);
-    else if (m == 2) route_rows_kernel<EPL, 2><<<grid, block, 0, s>>>(a);
-    else route_rows_kernel<EPL, 4><<<grid, block, 0, s>>>(a);
+bool launch_rows(const RouteArgs& a, int m, dim3 grid, dim3 block, hipStream_t s) {
+  if (m == 0) {
+    route_rows_kernel<EPL, 0><<<grid, block, 0, s>>>(a);
+    return true;
   }
+  if constexpr (EPL >= 8) {  // G = EPL / m groups, at most 16 (one per lane of a row)
+    if constexpr (EPL <= kRowLanes) {
+      if (m == 1) {
+        route_rows_kernel<EPL, 1><<<grid, block, 0, s>>>(a);
+        return true;
+      }
+    }
+    if (m == 2) route_rows_kernel<EPL, 2><<<grid, block, 0, s>>>(a);
+    else if (m == 4) route_rows_kernel<EPL, 4><<<grid, block, 0, s>>>(a);
+    else return false;
+    return true;
+  }
+  return false;
 }
 
 // Experts per lane of the row router for this configuration, or 0 when it does not apply.
@@ -545,15 +557,17 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   if (epl > 0) {
     const int per_block = kWavesPerBlock * kRowTokens;
     const dim3 grid((a.T + per_block - 1) / per_block), block(64 * kWavesPerBlock);
+    bool launched = false;
     switch (epl) {
-      case 1: launch_rows<1>(a, m, grid, block, s); break;
-      case 2: launch_rows<2>(a, m, grid, block, s); break;
-      case 4: launch_rows<4>(a, m, grid, block, s); break;
-      case 8: launch_rows<8>(a, m, grid, block, s); break;
-      case 16: launch_rows<16>(a, m, grid, block, s); break;
-      default: launch_rows<32>(a, m, grid, block, s); break;
+      case 1: launched = launch_rows<1>(a, m, grid, block, s); break;
+      case 2: launched = launch_rows<2>(a, m, grid, block, s); break;
+      case 4: launched = launch_rows<4>(a, m, grid, block, s); break;
+      case 8: launched = launch_rows<8>(a, m, grid, block, s); break;
+      case 16: launched = launch_rows<16>(a, m, grid, block, s); break;
+      default: launched = launch_rows<32>(a, m, grid, block, s); break;
     }
-    return hipGetLastError();
+    if (launched) return hipGetLastError();
+    // no instance for this shape: the one-token-per-wave kernel below covers every case
   }
   dim3 grid((a.T + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
   if (a.E <= 64) route_kernel<1><<<grid, block, 0, s>>>(a);
