@@ -165,10 +165,10 @@ size_t permute_workspace_bytes(int R, int E) {
 }
 
 int permute_chunk(int R) {
-  // at least 2048 routes per workgroup, and at most 64 workgroups
+  // at least 1024 routes per workgroup, and at most 64 workgroups
   int c = (R + 63) / 64;
-  c = (c + 1023) / 1024 * 1024;
-  return c < 2048 ? 2048 : c;
+  c = (c + 511) / 512 * 512;
+  return c < 1024 ? 1024 : c;
 }
 
 hipError_t launch_permute(const int32_t* ids, int R, int E, int32_t* offsets,
