@@ -1,6 +1,7 @@
 """Benchmark of the routed MoE FFN forward on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--no-ceilings]   # default workload: dsv3_bf16
     python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter scaling
 
 A step is one moe_ffn_forward over one batch: router, permute, grouped gate_up GEMM with
@@ -84,6 +85,66 @@ def copy_calibration():
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "copies": 5}),
           flush=True)
+
+
+def host_description() -> dict:
+    """CPU threads the oracle's BLAS uses (what the baseline actually ran on), the CPUs
+    this process may run on, and the CPU model."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cpus = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cores": _blas_threads(), "host_cpus": cpus, "cpu_model": model,
+            "os_cpu_count": os.cpu_count()}
+
+
+def measured_ceilings(reps: int = 5) -> dict:
+    """The device's attainable streaming-read bandwidth and dense bf16 MFMA rate, from the
+    probes of libmoe_probes.so (include/moe_probes.h), timed with HIP events on the
+    current stream: a 4 GiB read with 16-byte loads, and four independent
+    v_mfma_f32_32x32x16_bf16 chains per wave at two waves per SIMD. Best of `reps`."""
+    path = os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "libmoe_probes.so")
+    L = ctypes.CDLL(path)
+    L.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p]
+    L.moe_probe_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    grid = cus * 16
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+
+    def read():
+        rc = L.moe_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid, sh)
+        assert rc == 0, rc
+
+    t_read = min(time_launches(read, 1, stream) for _ in range(reps))
+    del buf
+    iters = 20000
+    mgrid = cus * 2  # 2 workgroups of four waves per CU: two waves per SIMD
+    fsink = torch.zeros(mgrid, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        rc = L.moe_probe_mfma_bf16(iters, fsink.data_ptr(), mgrid, sh)
+        assert rc == 0, rc
+
+    t_mfma = min(time_launches(mfma, 1, stream) for _ in range(reps))
+    flops = mgrid * 4 * iters * 4 * 2 * 32 * 32 * 16
+    return {"hbm_read_GBs": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
+            "source": "probes/ceilings.hip (4 GiB streaming read; bf16 32x32x16 MFMA loop)"}
 
 
 def log(*a):
@@ -262,7 +323,6 @@ def router_line(cfg, args):
     }
     if not args.no_cpu_baseline:
         import oracle.moe_oracle as O
-        threads = _blas_threads()
         logits = d["logits"].float().cpu().numpy().astype(np.float64)
         bias = None if d.get("correction_bias") is None else \
             d["correction_bias"].cpu().numpy().astype(np.float64)
@@ -274,8 +334,8 @@ def router_line(cfg, args):
                     bias)
             total += time.perf_counter() - t1
             done += n
-        line["cpu_baseline"] = {"value": done / total, "unit": "tokens/s", "cores": threads,
-                                "kind": "oracle",
+        line["cpu_baseline"] = {"value": done / total, "unit": "tokens/s",
+                                **host_description(), "kind": "oracle",
                                 "sample": f"first {n} of {cfg.T} tokens, repeated "
                                           f"({done} routed), float64 numpy oracle, {total:.1f} s"}
     print(json.dumps(line), flush=True)
@@ -333,7 +393,7 @@ def swiglu_line(cfg, args):
             total += time.perf_counter() - t1
             done += x.shape[0]
         line["cpu_baseline"] = {"value": done / total, "unit": "rows/s",
-                                "cores": _blas_threads(), "kind": "oracle",
+                                **host_description(), "kind": "oracle",
                                 "sample": f"first 512 of {cfg.rows} rows, repeated ({done} "
                                           f"rows), float64 numpy oracle, {total:.1f} s"}
     print(json.dumps(line), flush=True)
@@ -385,7 +445,7 @@ def layout_line(cfg, args):
                 O.pre_permute(h, ii, mc.E, cfg.layout, cfg.block_size)
                 total += time.perf_counter() - t1
                 done += ii.size
-            sample = {"value": done / total, "unit": "routes/s", "cores": _blas_threads(),
+            sample = {"value": done / total, "unit": "routes/s", **host_description(),
                       "kind": "oracle", "sample": f"first 512 of {mc.T} tokens ({ii.size} "
                       f"routes), repeated, float64 numpy oracle, {total:.1f} s"}
     else:
@@ -416,7 +476,7 @@ def layout_line(cfg, args):
                 total += time.perf_counter() - t1
                 done += int(cnt[e])
                 e += 1
-            sample = {"value": done / 8 / total, "unit": "tokens/s", "cores": _blas_threads(),
+            sample = {"value": done / 8 / total, "unit": "tokens/s", **host_description(),
                       "kind": "oracle", "sample": f"experts 0..{e - 1} of {fc.E} ({done} valid "
                       f"rows), float64 numpy oracle, {total:.1f} s"}
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
@@ -490,11 +550,6 @@ def fp8_line(cfg, args):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         import oracle.moe_oracle as O
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        except Exception:  # pragma: no cover
-            threads = os.cpu_count() or 1
         done, total, g = 0, 0.0, 0
         while total < args.cpu_budget / 2 and g < cfg.E:
             sub = {k: v[g:g + 1].cpu().numpy() for k, v in d.items() if k != "counts"}
@@ -505,7 +560,7 @@ def fp8_line(cfg, args):
             done += int(counts[g])
             g += 1
         line["cpu_baseline"] = {
-            "value": done / 8.0 / total, "unit": "tokens/s", "cores": int(threads),
+            "value": done / 8.0 / total, "unit": "tokens/s", **host_description(),
             "kind": "oracle",
             "sample": f"experts 0..{g - 1} of {cfg.E} ({done} of {rows} valid rows), float64 "
                       f"numpy oracle, {total:.1f} s"}
@@ -515,11 +570,6 @@ def fp8_line(cfg, args):
 def cpu_baseline(cfg, d, budget_s: float):
     """The CPU oracle, as it stands, on the first n tokens of the same workload."""
     import oracle.moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
     host = {k: (v.float().cpu().numpy() if v.is_floating_point() else v.cpu().numpy())
             for k, v in d.items()}
     kw = dict(top_k=cfg.K, scoring=cfg.scoring, renormalize=cfg.renormalize,
@@ -544,10 +594,11 @@ def cpu_baseline(cfg, d, budget_s: float):
                           host["w_down"], **kw)
         total += time.perf_counter() - t0
         passes += 1
-    return {"value": n * passes / total, "unit": "tokens/s", "cores": int(threads),
+    return {"value": n * passes / total, "unit": "tokens/s", **host_description(),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same workload, {passes} pass(es), "
-                      f"float64 numpy oracle, {total:.1f} s wall"}
+                      f"float64 numpy oracle (BLAS matmuls on 'cores' threads), "
+                      f"{total:.1f} s wall"}
 
 
 def main(argv=None):
@@ -555,7 +606,7 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_bf16",
+    ap.add_argument("--workload", default="dsv3_bf16",
                     choices=sorted(I.CONFIGS) + sorted(I.FP8_CONFIGS) + sorted(I.SWIGLU_CONFIGS)
                     + sorted(I.LAYOUT_CONFIGS))
     ap.add_argument("--backend", default="auto", choices=["auto", "staged", "indexed"])
@@ -563,6 +614,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured stream-read and MFMA-loop ceilings")
     ap.add_argument("--host-inputs", action="store_true",
                     help="FP8 workloads: replicate one host-generated expert (counter runs)")
     args = ap.parse_args(argv)
@@ -669,6 +722,21 @@ def main(argv=None):
                   "algorithmic_bytes": l_bytes, "flops": l_flops,
                   "distinct_experts": n_exp},
     }
+    # the benchmark spec's targets: 60 % of bf16 MFMA peak for prefill layers, 70 % of HBM
+    # bandwidth for decode layers (whole-layer fractions, next to the target)
+    if backend == "staged":
+        line["layer_mfma_frac"] = line["layer"]["mfma_frac"]
+        line["mfma_target"] = 0.60
+    else:
+        line["layer_hbm_frac"] = line["layer"]["hbm_frac"]
+        line["hbm_target"] = 0.70
+    if not args.no_ceilings:
+        log("[bench] measured ceilings")
+        ceil = measured_ceilings()
+        line["ceilings"] = ceil
+        c = ceil["hbm_read_GBs"] if roof["unit"] == "GB/s" else ceil["mfma_bf16_TFLOPs"]
+        line["roofline"]["measured_ceiling"] = c
+        line["roofline"]["frac_of_measured_ceiling"] = round(roof["achieved"] / c, 4)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_budget)

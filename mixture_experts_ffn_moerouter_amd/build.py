@@ -3,7 +3,8 @@
     python -m mixture_experts_ffn_moerouter_amd.build [--jobs N]
 
 Every HIP source under csrc/ is compiled to an object in csrc/_build/, in parallel, and
-linked into mixture_experts_ffn_moerouter_amd/libmoe.so. Packed-FP32 instructions are
+linked into mixture_experts_ffn_moerouter_amd/libmoe.so; the measurement probes under
+probes/ (include/moe_probes.h) are linked into libmoe_probes.so the same way. Packed-FP32 instructions are
 turned off for device code (-packed-fp32-ops): the compiler still emits scalar FP32.
 """
 import argparse
@@ -17,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBES = os.path.join(PKG, "probes")
+PROBE_LIB = os.path.join(PKG, "libmoe_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
@@ -32,10 +35,9 @@ def _run(cmd):
     return p.returncode, out
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
+def _compile_and_link(srcs, objdir, lib, jobs, verbose):
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
     cmds = [[HIPCC, *FLAGS, "-c", s, "-o", o] for s, o in zip(srcs, objs)]
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         results = list(ex.map(_run, cmds))
@@ -46,14 +48,22 @@ def build(jobs: int = 8, verbose: bool = False) -> str:
         if rc:
             print("FAILED: " + " ".join(cmd), file=sys.stderr)
             failed = True
+    name = os.path.basename(lib)
     if failed:
-        raise RuntimeError("libmoe.so: compilation failed")
-    tmp = LIB + ".tmp"
+        raise RuntimeError(name + ": compilation failed")
+    tmp = lib + ".tmp"
     rc, out = _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs])
     if rc:
         print(out, file=sys.stderr)
-        raise RuntimeError("libmoe.so: link failed")
-    os.replace(tmp, LIB)
+        raise RuntimeError(name + ": link failed")
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8, verbose: bool = False) -> str:
+    _compile_and_link(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), BUILD, LIB, jobs,
+                      verbose)
+    _compile_and_link(sorted(glob.glob(os.path.join(PROBES, "*.hip"))),
+                      os.path.join(PROBES, "_build"), PROBE_LIB, jobs, verbose)
     return LIB
 
 

@@ -289,6 +289,7 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
     offsets = (const int32_t*)workspace;
   }
   GemmArgs g;
+  g.tag = 0;
   g.a = a;
   g.a_rows = a_rows;
   g.a_rows_div = a_rows_div < 1 ? 1 : a_rows_div;
@@ -629,6 +630,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
   } else {
     // 3. gate_up GEMM + activation, A rows gathered from hidden by route
     GemmArgs g;
+    g.tag = 0;
     g.a = hidden;
     g.a_rows = sorted;
     g.a_rows_div = (int)K;
@@ -673,6 +675,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
   // 6. shared expert: one "expert" owning every token
   if (c.F_shared > 0) {
     GemmArgs g;
+    g.tag = 1;  // a separately named kernel instance in profiles
     g.a = hidden;
     g.a_rows = nullptr;
     g.a_rows_div = 1;

@@ -91,7 +91,9 @@ __device__ __forceinline__ float gated_f(int kind, float g, float l, float alpha
   return kind == 1 ? gelu_f(g) * l : swiglu_f(g, l, alpha, beta, limit);
 }
 
-template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT>
+// TAG only names the instance (1: the shared expert's launches), so a profile lists the
+// shared expert's GEMMs apart from the routed ones; the code is the same.
+template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
 __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   constexpr int LA = NS - 1;  // steps in flight ahead of the one multiplied
   __shared__ int s_tmp[kNT / 64];
@@ -450,7 +452,7 @@ int cu_count() {
   return v;
 }
 
-template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT>
+template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
 hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
   const int n_tiles_n = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
   const int64_t max_tiles = ((int64_t)g.M + kBMX - 1) / kBMX + (g.E < g.M ? g.E : g.M);
@@ -459,7 +461,7 @@ hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
   if (grid > cap) grid = cap;
   grid = (grid + kXcd - 1) / kXcd * kXcd;       // a multiple of the XCD count
   const size_t lds = (size_t)NS * kStage + kMapBytes;
-  const auto kern = gemm_h16_kernel<NS, ACT, LAYOUT, OUT_F32, DT>;
+  const auto kern = gemm_h16_kernel<NS, ACT, LAYOUT, OUT_F32, DT, TAG>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -469,14 +471,17 @@ hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
 
 // Three stages (two steps in flight) need at least two steps per tile; a single-step
 // contraction runs with two.
-template <bool ACT, int LAYOUT, bool OUT_F32, int DT>
+template <bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG = 0>
 hipError_t launch_h16_act(const GemmArgs& g, hipStream_t s) {
-  if (g.Kd > kBK) return launch_h16_ns<3, ACT, LAYOUT, OUT_F32, DT>(g, s);
-  return launch_h16_ns<2, ACT, LAYOUT, OUT_F32, DT>(g, s);
+  if (g.Kd > kBK) return launch_h16_ns<3, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  return launch_h16_ns<2, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
 }
 
 template <int DT>
 hipError_t launch_h16(const GemmArgs& g, hipStream_t s) {
+  if (g.tag == 1 && g.out_dt == g.dt && (!g.act || g.layout == 0))  // the shared expert
+    return g.act ? launch_h16_act<true, 0, false, DT, 1>(g, s)
+                 : launch_h16_act<false, 0, false, DT, 1>(g, s);
   if (g.act) {
     if (g.layout == 0)
       return g.out_dt == 0 ? launch_h16_act<true, 0, true, DT>(g, s)

@@ -138,6 +138,7 @@ struct GemmArgs {
   void* out;          // [M, Nout]
   int Nout;           // Nw or Nw/2
   int dt, out_dt;
+  int tag;            // 1: the shared expert's launch (a separately named kernel instance)
 };
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
 

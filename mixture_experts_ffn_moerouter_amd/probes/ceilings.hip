@@ -1,0 +1,75 @@
+// Measurement instruments (include/moe_probes.h): the attainable streaming-read bandwidth
+// and the attainable dense bf16 matrix-core rate of the device, measured by the benchmark
+// beside the published peaks. Not part of the MoE path.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_probes.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kThreads = 256;
+constexpr int kMagic = 0x5a5a1234;  // a checksum ordinary probe data does not produce
+
+// Each thread reads 16-byte vectors i, i + S, i + 2S, ... (S = grid threads), four loads
+// in flight per iteration, and folds them into a checksum.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const i32x4* __restrict__ src,
+                                                               int64_t n, int32_t* sink) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  i32x4 acc = {0, 0, 0, 0};
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const i32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
+                d = src[i + 3 * stride];
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n; i += stride) acc ^= src[i];
+  const int v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (v == kMagic) sink[blockIdx.x] = v;
+}
+
+// Four independent accumulator chains per wave; operands come from the thread index so
+// they are not constants.
+__global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int64_t iters, float* sink) {
+  const short t = (short)threadIdx.x;
+  bf16x8 a, b;
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (short)(0x3c00 + ((t + j) & 7));   // small positive bf16 values
+    b[j] = (short)(0x3b80 + ((t * 3 + j) & 7));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int64_t k = 0; k < iters; ++k) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int j = 0; j < 16; ++j) s += c0[j] + c1[j] + c2[j] + c3[j];
+  if (s == -1.0f) sink[blockIdx.x] = s;  // the sums are positive
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_probe_stream_read(const void* src, int64_t bytes, int32_t* sink, int32_t grid,
+                          void* stream) {
+  if (!src || !sink || grid < 1 || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15))
+    return (int)hipErrorInvalidValue;
+  stream_read_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>((const i32x4*)src,
+                                                                  bytes / 16, sink);
+  return (int)hipGetLastError();
+}
+
+int moe_probe_mfma_bf16(int64_t iters, float* sink, int32_t grid, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  mfma_bf16_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>(iters, sink);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

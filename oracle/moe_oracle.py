@@ -32,7 +32,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "FORMATS", "round_to", "sigmoid", "scores", "ranked", "select_experts",
+    "FORMATS", "round_to", "sigmoid", "scores", "ranked", "selection_keys", "select_experts",
     "routing_weights", "ep_router_outputs", "RouteResult", "route", "swiglu", "gelu",
     "gated", "swiglu_op", "ACTIVATIONS", "split_gate_up", "expert_mlp", "grouped_gemm",
     "grouped_gemm_act",
@@ -116,22 +116,16 @@ def ranked(values) -> np.ndarray:
     return np.lexsort((np.arange(v.size), -v))
 
 
-def select_experts(s, top_k: int, correction_bias=None, num_expert_group: int = 1,
-                   topk_group: int = 1):
-    """Top-k selection in float32, with optional bias and group limit.
+def selection_keys(s, correction_bias=None, num_expert_group: int = 1):
+    """The float32 selection keys and group scores the top-k compares.
 
-    [MR] MoERouter (selection topk | noaux_tc, where noaux_tc adds the bias before the
-    top-k); [TO] FusedMoEFwdOp and FusedTopKFwdOp (DeepSeek-V3 grouped routing).
+    [MR] MoERouter (noaux_tc adds the bias to the scores before the top-k); [TO]
+    FusedMoEFwdOp and FusedTopKFwdOp (DeepSeek-V3 grouped routing).
 
-    u_e = f32(s_e) or f32(f32(s_e) + bias_e). With G groups of E/G consecutive experts,
-    a group's score is f32(largest u + second largest u) when a bias is given, and its
-    largest score otherwise; the topk_group best groups stay eligible. The K eligible
-    experts with the largest u are returned in (u descending, index ascending) order.
-
-    Also returns the near-tie diagnostics: gap_sel[t], the smallest difference between
-    consecutive keys among the K+1 best eligible experts (it covers the kept/dropped
-    boundary and the order inside the row), and gap_group[t], the difference between
-    the last kept and the first dropped group score (inf without groups).
+    u_e = f32(s_e), or f32(f32(s_e) + f32(bias_e)) with a bias. With G groups of E/G
+    consecutive experts, a group's score is f32(largest u + second largest u) when a bias
+    is given (a group of one expert: its single u), and its largest score otherwise.
+    Returns (u [T,E], gs [T,G]); gs is None without groups.
     """
     s32 = round_to(s, "f32")
     T, E = s32.shape
@@ -140,6 +134,36 @@ def select_experts(s, top_k: int, correction_bias=None, num_expert_group: int = 
     else:
         u = round_to(s32 + round_to(np.asarray(correction_bias, np.float64), "f32")[None, :],
                      "f32")
+    G = int(num_expert_group)
+    if G <= 1:
+        return u, None
+    ug = u.reshape(T, G, E // G)
+    if correction_bias is not None and E // G >= 2:
+        top2 = np.sort(ug, axis=2)[:, :, -2:]
+        gs = round_to(top2[:, :, 1] + top2[:, :, 0], "f32")
+    elif correction_bias is not None:
+        gs = ug[:, :, 0].copy()
+    else:
+        gs = ug.max(axis=2)
+    return u, gs
+
+
+def select_experts(s, top_k: int, correction_bias=None, num_expert_group: int = 1,
+                   topk_group: int = 1):
+    """Top-k selection in float32, with optional bias and group limit.
+
+    [MR] MoERouter (selection topk | noaux_tc); [TO] FusedMoEFwdOp and FusedTopKFwdOp.
+    The keys and group scores are those of selection_keys(); the topk_group best groups
+    (ties to the lower group) stay eligible, and the K eligible experts with the largest
+    key are returned in (key descending, index ascending) order.
+
+    Also returns the near-tie diagnostics: gap_sel[t], the smallest difference between
+    consecutive keys among the K+1 best eligible experts (it covers the kept/dropped
+    boundary and the order inside the row), and gap_group[t], the difference between
+    the last kept and the first dropped group score (inf without groups).
+    """
+    u, gs_all = selection_keys(s, correction_bias, num_expert_group)
+    T, E = u.shape
     G, TG, K = int(num_expert_group), int(topk_group), int(top_k)
     group_of = np.arange(E) // (E // G)
     sel = np.zeros((T, K), dtype=np.int64)
@@ -148,14 +172,7 @@ def select_experts(s, top_k: int, correction_bias=None, num_expert_group: int = 
     for t in range(T):
         eligible = np.ones(E, dtype=bool)
         if G > 1:
-            ug = u[t].reshape(G, E // G)
-            if correction_bias is not None and E // G >= 2:
-                top2 = np.sort(ug, axis=1)[:, -2:]
-                gs = round_to(top2[:, 1] + top2[:, 0], "f32")
-            elif correction_bias is not None:
-                gs = ug[:, 0].copy()
-            else:
-                gs = ug.max(axis=1)
+            gs = gs_all[t]
             gorder = ranked(gs)
             eligible = np.isin(group_of, gorder[:TG])
             if TG < G:
@@ -218,6 +235,8 @@ class RouteResult:
     gap_group: np.ndarray     # [T]
     router_probs: Optional[np.ndarray] = None
     weight_scale: Optional[np.ndarray] = None
+    keys: Optional[np.ndarray] = None          # [T,E] float32 selection keys (diagnostic)
+    group_scores: Optional[np.ndarray] = None  # [T,G] group scores, None without groups
 
 
 def route(logits, top_k: int, scoring: str = "softmax", renormalize: bool = False,
@@ -242,6 +261,7 @@ def route(logits, top_k: int, scoring: str = "softmax", renormalize: bool = Fals
                                                  num_expert_group, topk_group)
     wn, w = routing_weights(s, sel, renormalize, routed_scaling_factor)
     res = RouteResult(s, sel, wn, round_to(w, "f32"), gap_sel, gap_group)
+    res.keys, res.group_scores = selection_keys(s, correction_bias, num_expert_group)
     if router_probs_dtype is not None:
         count = s.shape[1] - local_expert_start if local_expert_count is None \
             else local_expert_count

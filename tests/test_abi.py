@@ -265,3 +265,24 @@ def test_layout_argument_errors():
     assert gl(layout=2, max_m=-1) == B.MOE_ERR_INVALID_ARG
     assert gl(layout=0, N=63, act_=ctypes.byref(act)) == B.MOE_ERR_INVALID_ARG
     assert B.lib().moe_grouped_gemm_layout_workspace_size(4) >= 32
+
+
+def test_probe_library_exports_its_symbols():
+    """libmoe_probes.so (measurement instruments for the bench's ceilings) exports what
+    include/moe_probes.h declares, and refuses bad sizes on the host."""
+    hdr = os.path.join(os.path.dirname(HEADER), "moe_probes.h")
+    text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\s*\(", text, re.M)))
+    assert names == ["moe_probe_mfma_bf16", "moe_probe_stream_read"], names
+    path = os.path.join(os.path.dirname(B.LIB_PATH), "libmoe_probes.so")
+    L = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(L, n), n
+    L.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int32, ctypes.c_void_p]
+    L.moe_probe_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p]
+    # host-side refusals return before any launch (hipErrorInvalidValue = 1)
+    assert L.moe_probe_stream_read(None, 1024, None, 1, None) == 1
+    assert L.moe_probe_stream_read(16, 1000, 16, 1, None) == 1
+    assert L.moe_probe_mfma_bf16(0, 16, 1, None) == 1

@@ -14,7 +14,7 @@ import bench  # noqa: E402
 REQUIRED = {"metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
             "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config"}
 ROOF = {"bound", "achieved", "peak", "unit", "frac", "traffic"}
-CPU = {"value", "unit", "cores", "kind", "sample"}
+CPU = {"value", "unit", "cores", "host_cpus", "cpu_model", "kind", "sample"}
 
 
 def _line(capsys, argv):
@@ -56,6 +56,11 @@ def test_bench_line_full_size(capsys, workload):
                           "--kernel-reps", "2", "--no-cpu-baseline"])
     _check(line, 2, 1, workload)
     assert "cpu_baseline" not in line
+    if workload == "qwen3_bf16":  # a layer line: targets and the measured ceilings
+        assert line["mfma_target"] == 0.60 and 0 < line["layer_mfma_frac"] < 1
+        c = line["ceilings"]
+        assert 1000 < c["hbm_read_GBs"] < 8000 and 500 < c["mfma_bf16_TFLOPs"] < 2600
+        assert line["roofline"]["measured_ceiling"] > 0
 
 
 def test_bench_refuses_several_gpus(capsys):

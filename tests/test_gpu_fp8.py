@@ -144,26 +144,44 @@ def test_fp8_guard_bands_and_repeat():
     assert torch.equal(first, out)
 
 
-def test_fp8_full_size_sampled():
-    """The DeepSeek-V3 gate_up shape (E 256, slabs of 256 rows, K 7168, N 4096): every
-    output computed on the GPU, sampled rows of three experts checked."""
-    cfg = I.FP8_CONFIGS["dsv3_fp8_gate_up"]
+def boundary_rows(m: int, stride: int = 32) -> np.ndarray:
+    """Rows 0 and m - 1 and both sides of every stride-row boundary below m: the first
+    and last row of any row tile whose height is a multiple of stride."""
+    j = np.arange(stride, m, stride)
+    return np.unique(np.concatenate([[0, m - 1], j - 1, j])).astype(np.int64)
+
+
+@pytest.mark.parametrize("name", ["dsv3_fp8_gate_up", "dsv3_fp8_down"])
+def test_fp8_full_size_every_expert(name):
+    """The DeepSeek-V3 shapes over masked slabs (E 256, slabs of 256 rows, about 128 valid
+    rows per expert): every output computed on the GPU. For every expert, its boundary
+    rows (first and last row of every row tile) are compared on one 256-column weight
+    tile (expert g takes tile g mod N/256, so every weight tile is compared on 16 or more
+    experts), and its rows past the count must be untouched."""
+    cfg = I.FP8_CONFIGS[name]
     say(f"[fp8-full] {cfg.name} generating inputs")
     d = I.make_fp8_inputs(cfg, device="cuda")
     say(f"[fp8-full] {cfg.name} gemm")
     out = run(d)
     counts = d["counts"].cpu().numpy()
-    rng = np.random.default_rng(0)
-    for g in rng.choice(cfg.E, size=3, replace=False):
+    nt = cfg.N // 256
+    got_all, ref_all = [], []
+    for g in range(cfg.E):
         m = int(counts[g])
-        rows = np.sort(rng.choice(m, size=min(4, m), replace=False))
-        say(f"[fp8-full] expert {g} rows {rows.tolist()}")
-        sub = {"a": d["a"][g:g + 1, rows].cpu().numpy(),
-               "a_scale": d["a_scale"][g:g + 1, rows].cpu().numpy(),
-               "b": d["b"][g:g + 1].cpu().numpy(),
-               "b_scale": d["b_scale"][g:g + 1].cpu().numpy()}
+        if m == 0:
+            continue
+        rows = boundary_rows(m)
+        c0 = 256 * (g % nt)
+        rt = torch.as_tensor(rows, device="cuda")
+        sub = {"a": d["a"][g:g + 1, rt].cpu().numpy(),
+               "a_scale": d["a_scale"][g:g + 1, rt].cpu().numpy(),
+               "b": d["b"][g:g + 1, c0:c0 + 256].cpu().numpy(),
+               "b_scale": d["b_scale"][g:g + 1, c0 // 128:c0 // 128 + 2].cpu().numpy()}
         ref = O.grouped_gemm_fp8_masked(sub["a"], sub["a_scale"], sub["b"], sub["b_scale"],
-                                        np.array([len(rows)]))
-        got = np64(out[g:g + 1, rows])
-        check(got, ref, np.array([len(rows)]), cfg.K, f"{cfg.name} expert {g}")
-        assert np.all(np64(out[g, m:]) == SENTINEL)
+                                        np.array([rows.size]))
+        got = np64(out[g:g + 1, rt, c0:c0 + 256])
+        check(got, ref, np.array([rows.size]), cfg.K, f"{cfg.name} expert {g}")
+        assert np.all(np64(out[g, m:]) == SENTINEL), f"expert {g} wrote past its count"
+        got_all.append(got.ravel())
+        ref_all.append(ref.ravel())
+    assert_close(np.concatenate(got_all), np.concatenate(ref_all), "bf16", cfg.name)

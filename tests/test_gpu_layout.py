@@ -166,9 +166,11 @@ def test_layer_through_layout_ops(layout, arg):
         assert (inv_np < 0).any()
 
 
-def test_masked_bf16_gemm_full_size_sampled():
+def test_masked_bf16_gemm_full_size_every_expert():
     """The DeepSeek-V3 gate_up shape over a masked slab in bf16 (E 256, max_m 256, K 7168,
-    N 4096, about 128 rows per expert): every output on the GPU, sampled rows checked."""
+    N 4096, about 128 rows per expert): every output on the GPU; for every expert its
+    boundary rows (first and last row of every 32-row multiple tile) on all columns against
+    the oracle's grouped GEMM over the masked layout, and its rows past the count intact."""
     cfg = I.FP8_CONFIGS["dsv3_fp8_gate_up"]
     say("[gemm-layout-full] generating")
     g = torch.Generator(device="cuda").manual_seed(7)
@@ -181,9 +183,18 @@ def test_masked_bf16_gemm_full_size_sampled():
     B.moe_grouped_gemm_layout(a, w, "masked", counts, out=out)
     torch.cuda.synchronize()
     c = counts.cpu().numpy()
-    rng = np.random.default_rng(0)
-    for e in rng.choice(cfg.E, size=3, replace=False):
-        rows = np.sort(rng.choice(int(c[e]), size=4, replace=False))
-        ref = np64(a[e, rows]) @ np64(w[e]).T
-        assert_close(np64(out[e, rows]), O.round_to(ref, "bf16"), "bf16", f"expert {e}")
-        assert np.all(np64(out[e, int(c[e]):]) == SENTINEL)
+    got_all, ref_all = [], []
+    for e in range(cfg.E):
+        m = int(c[e])
+        if m == 0:
+            continue
+        j = np.arange(32, m, 32)
+        rows = torch.as_tensor(np.unique(np.concatenate([[0, m - 1], j - 1, j])), device="cuda")
+        ref = O.grouped_gemm_layout(np64(a[e:e + 1, rows]), [np64(w[e])], "masked",
+                                    np.array([rows.numel()]), out_dtype="bf16")
+        got = np64(out[e:e + 1, rows])
+        got_all.append(got.ravel())
+        ref_all.append(ref.ravel())
+        assert_close(got, ref, "bf16", f"expert {e}")
+        assert np.all(np64(out[e, m:]) == SENTINEL)
+    assert_close(np.concatenate(got_all), np.concatenate(ref_all), "bf16", "all experts")

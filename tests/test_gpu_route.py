@@ -6,7 +6,7 @@ import torch
 import oracle.moe_oracle as O
 from mixture_experts_ffn_moerouter_amd import binding as B
 from mixture_experts_ffn_moerouter_amd import inputs as I
-from moe_testlib import TOL, check_route, guarded, np64, say
+from moe_testlib import TOL, check_route, guarded, np64, route_rerouter, say
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +57,8 @@ def test_route_parity(name):
     r = O.route(np64(logits), K, scoring, renorm, rsf, G, TG,
                 None if cb is None else np64(cb),
                 None if ids_in is None else ids_in.cpu().numpy())
-    tie = check_route(w, ids, r, name)
+    tie, _ = check_route(w, ids, r, name, route_rerouter(np64(logits), K, scoring, renorm, rsf),
+                         G, TG)
     assert tie.mean() < 0.05, f"{name}: {tie.sum()} near-tie tokens"
 
 
@@ -73,19 +74,21 @@ def test_router_ep_outputs(dt, slice_, T):
                       local_expert_count=count, router_probs_dtype=dt)
     w, ids, rp, ws = B.moe_route(logits, cfg, with_router_probs=True)
     torch.cuda.synchronize()
-    r = O.route(np64(logits), K, "sqrt_softplus", True, 1.25, local_expert_start=start,
-                local_expert_count=count, router_probs_dtype=dt)
-    tie = check_route(w, ids, r, "ep")
-    ok = ~tie
-    got = np64(rp)[ok]
-    ref = r.router_probs[ok]
+    ep = dict(local_expert_start=start, local_expert_count=count, router_probs_dtype=dt)
+    r = O.route(np64(logits), K, "sqrt_softplus", True, 1.25, **ep)
+    # every token is compared: near-tie tokens against the oracle's outputs for the
+    # GPU's own (valid) choice
+    _, r = check_route(w, ids, r, "ep", route_rerouter(np64(logits), K, "sqrt_softplus",
+                                                       True, 1.25, **ep))
+    got = np64(rp)
+    ref = r.router_probs
     fill = O.round_to(-1e4 if dt == "f16" else -1e30, dt)
     assert np.array_equal(got == fill, ref == fill), "sentinel positions differ"
     assert np.all(got[ref == fill] == fill)
     m = ref != fill
     ulp = {"f32": 2.0 ** -23, "bf16": 2.0 ** -8, "f16": 2.0 ** -10}[dt]
     assert np.all(np.abs(got[m] - ref[m]) <= 2 * ulp * np.abs(ref[m]) + 1e-6)
-    gws, rws = np64(ws)[ok], r.weight_scale[ok]
+    gws, rws = np64(ws), r.weight_scale
     assert np.all((gws == 0) == (rws == 0)), "zero weight_scale differs"
     assert np.all(np.abs(gws - rws) <= 2 * ulp * np.abs(rws))
     if count == E:
@@ -101,9 +104,11 @@ def test_router_decode_pass():
                       local_expert_start=64, local_expert_count=64, router_probs_dtype="f16")
     w, ids, rp, ws = B.moe_route(d["logits"], cfg, with_router_probs=True)
     torch.cuda.synchronize()
-    r = O.route(np64(d["logits"]), cfg_.K, cfg_.scoring, cfg_.renormalize, cfg_.rsf,
-                local_expert_start=64, local_expert_count=64, router_probs_dtype="f16")
-    check_route(w, ids, r, "router_ep_f16")
+    ep = dict(local_expert_start=64, local_expert_count=64, router_probs_dtype="f16")
+    r = O.route(np64(d["logits"]), cfg_.K, cfg_.scoring, cfg_.renormalize, cfg_.rsf, **ep)
+    _, r = check_route(w, ids, r, "router_ep_f16",
+                       route_rerouter(np64(d["logits"]), cfg_.K, cfg_.scoring,
+                                      cfg_.renormalize, cfg_.rsf, **ep))
     assert np.array_equal(np64(rp) == -1e4, r.router_probs == -1e4)
     assert np.array_equal(np64(ws) == 0, r.weight_scale == 0)
 
@@ -151,6 +156,66 @@ def test_route_16bit_logits(ldt, scoring, groups, T):
     cfg = B.route_cfg(K, scoring, True, 2.5 if scoring == "sigmoid" else 1.0, G, TG)
     w, ids, _, _ = B.moe_route(logits, cfg, bias)
     torch.cuda.synchronize()
-    r = O.route(np64(logits), K, scoring, True, 2.5 if scoring == "sigmoid" else 1.0, G, TG,
+    rsf = 2.5 if scoring == "sigmoid" else 1.0
+    r = O.route(np64(logits), K, scoring, True, rsf, G, TG,
                 None if bias is None else np64(bias))
-    check_route(w, ids, r, f"{ldt} {scoring}")
+    check_route(w, ids, r, f"{ldt} {scoring}", route_rerouter(np64(logits), K, scoring, True, rsf),
+                G, TG)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("n_ranks", [2, 4, 8])
+@pytest.mark.parametrize("workload", ["dsv3_bf16", "decode_dsv3_bf16"])
+def test_fake_multi_rank(workload, n_ranks, dt):
+    """[MR] MoERouter, expert parallelism on one GPU: moe_route runs once per expert slice
+    [r E/n, (r+1) E/n), as each of n ranks would. Rank r's QMoE takes a softmax over its
+    router_probs row (its chosen local experts' w / W_local) and scales the result by
+    weight_scale (route_scale W_local), so summing weight_scale_r softmax(router_probs_r)
+    over the ranks must rebuild every global routing weight, and a rank with no chosen
+    expert adds nothing (weight_scale 0).
+
+    Bound: router_probs holds log(w) rounded to the dtype (relative error u: 2^-24, 2^-9,
+    2^-11), so each exp(router_probs) is off by at most |log w| u relative; the local
+    softmax's numerator and denominator together by 2 u max|log w| and the scale's
+    rounding by u: |rebuilt - w| <= 2 u (2 max|log w| + 1) |w| (float32: plus 1e-6
+    relative for the float32 arithmetic of the router)."""
+    cfg = I.CONFIGS[workload]
+    E, K = cfg.E, cfg.K
+    say(f"[route-ranks] {workload} n={n_ranks} dt={dt}")
+    d = I.make_router_inputs(cfg, device="cuda")
+    w_ref = ids_ref = None
+    parts = []
+    for r in range(n_ranks):
+        rc = B.route_cfg(K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG,
+                         local_expert_start=r * E // n_ranks,
+                         local_expert_count=E // n_ranks, router_probs_dtype=dt)
+        w, ids, rp, ws = B.moe_route(d["logits"], rc, d.get("correction_bias"),
+                                     with_router_probs=True)
+        torch.cuda.synchronize()
+        if w_ref is None:
+            w_ref, ids_ref = w, ids
+        else:  # the selection does not depend on the slice
+            assert torch.equal(ids, ids_ref) and torch.equal(w, w_ref)
+        parts.append((np64(rp), np64(ws)))
+    wg = w_ref.cpu().numpy().astype(np.float64)
+    ids = ids_ref.cpu().numpy().astype(np.int64)
+    T = wg.shape[0]
+    rebuilt = np.zeros_like(wg)
+    count = E // n_ranks
+    fill = O.round_to(-1e4 if dt == "f16" else -1e30, dt)
+    for r, (rp, ws) in enumerate(parts):
+        live = rp != fill
+        local = (ids >= r * count) & (ids < (r + 1) * count)
+        assert np.array_equal(live.sum(1), local.sum(1)), "filled columns differ from the ids"
+        assert np.all((ws == 0) == ~local.any(1)), "zero weight_scale where a route is local"
+        ex = np.where(live, np.exp(np.where(live, rp - rp.max(1, keepdims=True), 0.0)), 0.0)
+        soft = ex / np.maximum(ex.sum(1, keepdims=True), 1e-300)
+        for k in range(K):
+            m = local[:, k]
+            rebuilt[m, k] += ws[m] * soft[np.nonzero(m)[0], ids[m, k] - r * count]
+    u = {"f32": 2.0 ** -24, "bf16": 2.0 ** -9, "f16": 2.0 ** -11}[dt]
+    wn = wg / cfg.rsf
+    maxlog = np.abs(np.log(wn)).max(1, keepdims=True)
+    bound = 2 * u * (2 * maxlog + 1) * np.abs(wg) + (1e-6 * np.abs(wg) if dt == "f32" else 0)
+    err = np.abs(rebuilt - wg)
+    assert np.all(err <= bound), f"max excess {(err - bound).max():.3e} (T {T})"
