@@ -58,18 +58,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
 constexpr int kNT = 512;                // 8 waves: 2 (token rows) x 4 (weight rows)
-constexpr int kBMX = 128;               // token rows per tile
 constexpr int kBNW = 256;               // weight rows per tile
 constexpr int kBK = 64;                 // K elements per step (128 bytes of a row)
-constexpr int kPA = kBMX / 64;          // 1 KB transfers per wave and step: token rows
-constexpr int kPB = kBNW / 64;          //   and weight rows
-constexpr int kPieces = kPA + kPB;
-constexpr int kStage = (kBMX + kBNW) * 128;
-constexpr int kMaxE = 1024;
-constexpr int kMapBytes = 3 * (kMaxE + 1) * (int)sizeof(int);
+constexpr int kPB = kBNW / 64;          // 1 KB transfers of weight rows per wave and step
 constexpr int kXcd = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
-static_assert(3 * kStage + kMapBytes <= 160 * 1024, "LDS");
+constexpr int kLds = 160 * 1024;        // LDS per workgroup
+// Token rows per tile: BM = 160 (one tile holds an expert of up to 160 rows) when the
+// stages and the tile map fit in LDS, else 128.
+constexpr int stage_bytes(int bm) { return (bm + kBNW) * 128; }
+constexpr int map_bytes(int E) { return 3 * (E + 1) * (int)sizeof(int); }
+constexpr int kStaticLds = 64;          // s_tmp and alignment
 
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
@@ -93,18 +92,24 @@ __device__ __forceinline__ float gated_f(int kind, float g, float l, float alpha
 
 // TAG only names the instance (1: the shared expert's launches), so a profile lists the
 // shared expert's GEMMs apart from the routed ones; the code is the same.
-template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
+template <int NS, int BM, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
 __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
-  constexpr int LA = NS - 1;  // steps in flight ahead of the one multiplied
+  constexpr int LA = NS - 1;          // steps in flight ahead of the one multiplied
+  constexpr int kPA = (BM + 63) / 64;  // 1 KB transfers of token rows per wave and step
+  constexpr int kNPA = BM / 8;         // distinct ones (a wave past them repeats the last)
+  constexpr int kPieces = kPA + kPB;
+  constexpr int kStage = stage_bytes(BM);
+  constexpr int kNI = BM / 32;         // 16-row blocks per wave
+  static_assert(BM % 32 == 0 && kNPA <= 8 * kPA, "tile rows");
   __shared__ int s_tmp[kNT / 64];
   extern __shared__ __align__(16) uint8_t smem[];  // [NS][kStage], then the tile map
+  const int E = g.E;
   int* s_start = (int*)(smem + NS * kStage);
-  int* s_len = s_start + kMaxE + 1;
-  int* s_pre = s_len + kMaxE + 1;
+  int* s_len = s_start + E + 1;
+  int* s_pre = s_len + E + 1;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int E = g.E;
-  build_tile_map_segments<kNT>(g.seg_mode, g.offsets, E, g.M, g.max_m, kBMX, s_start, s_len,
+  build_tile_map_segments<kNT>(g.seg_mode, g.offsets, E, g.M, g.max_m, BM, s_start, s_len,
                                s_pre, s_tmp);
   const int n_tiles_n = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
   const int n_valid = s_pre[E] * n_tiles_n;
@@ -125,14 +130,16 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     const int t_e = s_pre[e + 1] - s_pre[e];
     const int local = L - s_pre[e] * n_tiles_n;
     nt = __builtin_amdgcn_readfirstlane(local / t_e);
-    const int rpt = rows_per_tile(s_len[e], kBMX);
+    const int rpt = rows_per_tile(s_len[e], BM);
     m0 = __builtin_amdgcn_readfirstlane(s_start[e] + (local % t_e) * rpt);
     m1 = __builtin_amdgcn_readfirstlane(min(m0 + rpt, s_start[e] + s_len[e]));
   };
 
-  // Transfers: wave w moves 1 KB pieces kPA w + u of the token rows (rows 16 w .. 16 w + 15)
-  // and kPB w + u of the weight rows (rows 32 w .. 32 w + 31); lane l takes row l / 8 of
-  // the piece and its 16-byte part (l % 8) ^ (row % 8).
+  // Transfers: wave w moves 1 KB pieces kPA w + u of the token rows (piece q holds rows
+  // 8 q .. 8 q + 7; a wave whose pieces run past the tile's kNPA repeats the last one, so
+  // every wave issues the same count) and kPB w + u of the weight rows (rows 32 w ..
+  // 32 w + 31); lane l takes row l / 8 of the piece and its 16-byte part (l % 8) ^ (row % 8).
+  auto apiece = [&](int u) { return min(kPA * wave + u, kNPA - 1); };
   const int prow = lane >> 3;
   const int kel = 8 * ((lane & 7) ^ prow);  // first K element of the lane's part
   const uint32_t pbyte = 2u * (uint32_t)kel;
@@ -144,7 +151,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     const int rows = m1 - m0;
 #pragma unroll
     for (int u = 0; u < kPA; ++u) {
-      const int r = 8 * (kPA * wave + u) + prow;
+      const int r = 8 * apiece(u) + prow;
       const bool on = r < rows;
       const int m = m0 + (on ? r : 0);
       const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
@@ -184,21 +191,22 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     const uint32_t kbyte = (uint32_t)k0 * 2u;
     if (p < kPA) {
       const uint32_t o = nxt ? aN[p] : aC[p];
-      dma16(ra, st + (kPA * wave + p) * 1024, in ? o + kbyte : kOOB);
+      dma16(ra, st + apiece(p) * 1024, in ? o + kbyte : kOOB);
     } else {
       const uint32_t o = nxt ? bN[p - kPA] : bC[p - kPA];
-      dma16(nxt ? rbN : rbC, st + kBMX * 128 + (kPB * wave + p - kPA) * 1024,
+      dma16(nxt ? rbN : rbC, st + BM * 128 + (kPB * wave + p - kPA) * 1024,
             in ? o + kbyte : kOOB);
     }
   };
 
-  // Wave (wm, wn): token 16-row blocks rowblk(i) = (wm + 2 (i / 2)) 32 + 16 (i % 2), weight
-  // rows wn 64 + 16 j. Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
+  // Wave (wm, wn): token 16-row blocks rowblk(i) = (2 i + wm) 16 (the two row waves take
+  // alternate blocks, so a partly filled tile stays balanced), weight rows wn 64 + 16 j.
+  // Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, lq = lane >> 4;
   const uint32_t fo0 = 16u * (uint32_t)(lq ^ (lr & 7));
   const uint32_t fo1 = 16u * (uint32_t)((lq ^ 4) ^ (lr & 7));
-  auto rowblk = [&](int i) { return (wm + 2 * (i >> 1)) * 32 + 16 * (i & 1); };
+  auto rowblk = [&](int i) { return (2 * i + wm) * 16; };
 
 #pragma unroll
   for (int q = 0; q < LA; ++q)
@@ -221,15 +229,16 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
       rbN = rbC;
     }
     const int e = te, nt = tnt, m0 = tm0, m1 = tm1;
-    const int nb = (m1 - m0 + 31) / 32;               // live 32-row blocks of the tile
+    const int nb = (m1 - m0 + 15) / 16;               // live 16-row blocks of the tile
     const int nbw = nb > wm ? (nb - wm + 1) / 2 : 0;  // ... and of this wave
-    f32x4 acc[4][4];
+    f32x4 acc[kNI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
-    // The K loop, compiled for 4 and for 2 live 16-row blocks of the wave.
+    // The K loop, compiled for kNI and for kNI - 2 live 16-row blocks of the wave (blocks
+    // past the live ones multiply zeros and are not stored).
     auto main_loop = [&](auto ni_c) {
       constexpr int NI = decltype(ni_c)::value;
       constexpr int NB = NI * 8;  // MFMAs per step
@@ -243,7 +252,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
                      : "memory");
         const int s = gs + k;
         const uint8_t* st = smem + (s % NS) * kStage;
-        const uint8_t* sb = st + kBMX * 128;
+        const uint8_t* sb = st + BM * 128;
         const int s2 = (s + LA) % NS;
         const bool nxt = k + LA >= nk;
         const int kk = nxt ? k + LA - nk : k + LA;
@@ -275,8 +284,8 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         }
       }
     };
-    if (nbw >= 2) main_loop(std::integral_constant<int, 4>{});
-    else main_loop(std::integral_constant<int, 2>{});
+    if (nbw > kNI - 2) main_loop(std::integral_constant<int, kNI>{});
+    else main_loop(std::integral_constant<int, kNI - 2>{});
     gs += nk;
 
     // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
@@ -319,9 +328,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
             }
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kNI; ++i) {
             const int m = m0 + rowblk(i) + lr;
-            if (i < 2 * nbw && m < m1) {
+            if (i < nbw && m < m1) {
               float v[4];
 #pragma unroll
               for (int c = 0; c < 4; ++c)
@@ -345,9 +354,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
               bn[c] = h16_to_f32<DT>(bias[(int64_t)e * g.Nw + min(n0 + c, g.Nw - 1)]);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < kNI; ++i) {
             const int m = m0 + rowblk(i) + lr;
-            if (i < 2 * nbw && m < m1) {
+            if (i < nbw && m < m1) {
               float v[4];
 #pragma unroll
               for (int c = 0; c < 4; ++c) v[c] = acc[i][j][c] + bn[c];
@@ -452,16 +461,16 @@ int cu_count() {
   return v;
 }
 
-template <int NS, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
+template <int NS, int BM, bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG>
 hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
   const int n_tiles_n = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
-  const int64_t max_tiles = ((int64_t)g.M + kBMX - 1) / kBMX + (g.E < g.M ? g.E : g.M);
+  const int64_t max_tiles = ((int64_t)g.M + BM - 1) / BM + (g.E < g.M ? g.E : g.M);
   int64_t grid = max_tiles * n_tiles_n;
   const int64_t cap = cu_count() / kXcd * kXcd;  // one workgroup per CU
   if (grid > cap) grid = cap;
   grid = (grid + kXcd - 1) / kXcd * kXcd;       // a multiple of the XCD count
-  const size_t lds = (size_t)NS * kStage + kMapBytes;
-  const auto kern = gemm_h16_kernel<NS, ACT, LAYOUT, OUT_F32, DT, TAG>;
+  const size_t lds = (size_t)NS * stage_bytes(BM) + map_bytes(g.E);
+  const auto kern = gemm_h16_kernel<NS, BM, ACT, LAYOUT, OUT_F32, DT, TAG>;
   hipError_t err = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -471,11 +480,16 @@ hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
 
 // Three stages (two steps in flight) need at least two steps per tile; a single-step
 // contraction runs with two.
+// 160-row tiles need three stages and the tile map of E experts in LDS (E up to 335);
+// otherwise 128-row tiles (E up to 1024).
 template <bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG = 0>
 hipError_t launch_h16_act(const GemmArgs& g, hipStream_t s) {
-  if (g.Kd > kBK) return launch_h16_ns<3, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
-  return launch_h16_ns<2, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  if (g.Kd <= kBK) return launch_h16_ns<2, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  if (3 * stage_bytes(160) + map_bytes(g.E) + kStaticLds <= kLds)
+    return launch_h16_ns<3, 160, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  return launch_h16_ns<3, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
 }
+static_assert(3 * stage_bytes(128) + map_bytes(1024) + kStaticLds <= kLds, "LDS");
 
 template <int DT>
 hipError_t launch_h16(const GemmArgs& g, hipStream_t s) {

@@ -21,6 +21,8 @@ SEGMENTS = {
     "one_expert_many_tiles": [1000],
     "tiny": [3, 0, 5],
     "uniform256": [256] * 12,
+    # around the 160-row tile: one tile up to 160 rows, two from 161
+    "around160": [160, 161, 159, 320, 321, 33, 0, 480],
 }
 
 
