@@ -18,8 +18,9 @@
  *     synchronise). Device-side metadata (expert ids, offsets) outside its stated
  *     range is a precondition violation, not an error that is reported.
  *   - Ownership: the caller owns every buffer, including workspaces. The library
- *     allocates no device memory and keeps no mutable global state; calls on one
- *     stream are ordered, calls on different streams must not share output buffers.
+ *     allocates no device memory and keeps no mutable global state, apart from the
+ *     fixed device scratch of moe_ffn_forward_noalloc; calls on one stream are
+ *     ordered, calls on different streams must not share output buffers.
  *   - Errors: every argument check runs on the host before anything is enqueued; a
  *     call that returns an error has launched nothing and written nothing. An output
  *     that overlaps an input returns MOE_ERR_OVERLAP before any write ([TO]
@@ -399,6 +400,32 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
                     const void* shared_w_down, void* out, void* shared_out,
                     float* topk_weights_out, int32_t* topk_ids_out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_ffn_forward_noalloc - moe_ffn_forward with the library's own fixed scratch in
+ * place of the caller's workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). It allocates nothing: no hipMalloc, hipFree or allocating library call.
+ *
+ * Arguments, results and errors are those of moe_ffn_forward without the workspace.
+ * The scratch is one static device array of MOE_FFN_NOALLOC_SCRATCH_BYTES in the
+ * library, one copy per GPU, held until the process ends; its address is resolved once
+ * per device on the first call made with that device current. A cfg whose
+ * moe_ffn_workspace_size exceeds that size returns MOE_ERR_WORKSPACE before anything is
+ * enqueued (64 MiB covers, e.g., decode batches of the DeepSeek-V3 shapes, the
+ * DeepSeek-V3 shapes up to about 250 tokens and the Qwen3 shapes up to about 860).
+ * Every call on a GPU uses the same array, and nothing in it needs to start at zero
+ * (each call writes every region before reading it): calls that overlap in time on one
+ * GPU (different streams, or different host threads) race on it and must be
+ * serialised by the caller.
+ * ------------------------------------------------------------------------------- */
+#define MOE_FFN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_ffn_forward_noalloc(const moe_ffn_cfg* cfg, const void* hidden, const void* logits,
+                            const float* correction_bias, const int32_t* expert_ids,
+                            const void* w_gate_up, const void* w_down, const void* b_gate_up,
+                            const void* b_down, const void* shared_w_gate_up,
+                            const void* shared_w_down, void* out, void* shared_out,
+                            float* topk_weights_out, int32_t* topk_ids_out, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_grouped_gemm_fp8_masked - block-scaled FP8 GEMM per expert over a masked slab:

@@ -36,7 +36,9 @@ SYMBOLS = ("moe_status_str", "moe_abi_version", "moe_route", "moe_permute_worksp
            "moe_ffn_workspace_size", "moe_ffn_backend", "moe_ffn_forward",
            "moe_grouped_gemm_fp8_masked", "moe_swiglu", "moe_grouped_gemm_layout_workspace_size",
            "moe_grouped_gemm_layout", "moe_layout_workspace_size", "moe_permute_align",
-           "moe_pre_permute")
+           "moe_pre_permute", "moe_ffn_forward_noalloc")
+# moe_ffn_forward_noalloc's fixed scratch (MOE_FFN_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeRouteCfg(ctypes.Structure):
@@ -130,6 +132,8 @@ def lib():
         L.moe_ffn_forward.restype = ctypes.c_int
         L.moe_ffn_forward.argtypes = [ctypes.POINTER(MoeFfnCfg)] + [_P] * 15 + \
             [ctypes.c_size_t, _P]
+        L.moe_ffn_forward_noalloc.restype = ctypes.c_int
+        L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(MoeFfnCfg)] + [_P] * 15
         _lib = L
     return _lib
 
@@ -420,4 +424,26 @@ def moe_ffn_forward(cfg: MoeFfnCfg, hidden, logits, w_gate_up, w_down, correctio
         _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(out), _ptr(shared_out),
         _ptr(topk_weights_out), _ptr(topk_ids_out), _ptr(workspace), workspace.numel(),
         _stream(stream)))
+    return out, shared_out
+
+
+def moe_ffn_forward_noalloc(cfg: MoeFfnCfg, hidden, logits, w_gate_up, w_down,
+                            correction_bias=None, expert_ids=None, b_gate_up=None, b_down=None,
+                            shared_w_gate_up=None, shared_w_down=None, out=None,
+                            shared_out=None, topk_weights_out=None, topk_ids_out=None,
+                            stream=None):
+    """moe_ffn_forward on the library's fixed scratch (no workspace argument; the library
+    allocates nothing). Outputs the caller omits are still allocated here by torch."""
+    T, H = hidden.shape
+    dev = hidden.device
+    cfg = MoeFfnCfg.from_buffer_copy(cfg)
+    cfg.route.logits_dtype = TORCH_DTYPES[logits.dtype]
+    out = torch.empty((T, H), dtype=hidden.dtype, device=dev) if out is None else out
+    if cfg.F_shared > 0 and shared_out is None:
+        shared_out = torch.empty((T, H), dtype=hidden.dtype, device=dev)
+    _check("moe_ffn_forward_noalloc", lib().moe_ffn_forward_noalloc(
+        ctypes.byref(cfg), _ptr(hidden), _ptr(logits), _ptr(correction_bias),
+        _ptr(expert_ids), _ptr(w_gate_up), _ptr(w_down), _ptr(b_gate_up), _ptr(b_down),
+        _ptr(shared_w_gate_up), _ptr(shared_w_down), _ptr(out), _ptr(shared_out),
+        _ptr(topk_weights_out), _ptr(topk_ids_out), _stream(stream)))
     return out, shared_out

@@ -2,8 +2,15 @@
 // launch order of each entry point declared in include/moe.h.
 #include <string.h>
 
+#include <atomic>
+
 #include "moe.h"
 #include "moe_internal.h"
+
+// Scratch of moe_ffn_forward_noalloc: a fixed device array, one copy per GPU. Host code
+// never uses this name as an address (on the host it is only a handle for the runtime);
+// the device address comes from hipGetSymbolAddress, resolved per device.
+static __device__ __align__(256) unsigned char scratch[MOE_FFN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -155,6 +162,23 @@ int backend_for(const moe_ffn_cfg& c, bool has_bias) {
   if (c.backend == MOE_BACKEND_INDEXED) return indexed_shape ? MOE_BACKEND_INDEXED : -1;
   return (c.T * c.route.top_k <= 2 * c.E && indexed_shape) ? MOE_BACKEND_INDEXED
                                                          : MOE_BACKEND_STAGED;
+}
+
+// Device address of `scratch` on the current device: hipGetSymbolAddress once per
+// device (with that device current), then the cached value. nullptr if it fails.
+void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cached[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  if (dev < kMaxDevices) {
+    void* p = cached[dev].load(std::memory_order_acquire);
+    if (p) return p;
+  }
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  if (dev < kMaxDevices) cached[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -710,6 +734,23 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
     if ((st = status_of(launch_grouped_gemm(d, strm)))) return st;
   }
   return MOE_OK;
+}
+
+int moe_ffn_forward_noalloc(const moe_ffn_cfg* cfg, const void* hidden, const void* logits,
+                            const float* correction_bias, const int32_t* expert_ids,
+                            const void* w_gate_up, const void* w_down, const void* b_gate_up,
+                            const void* b_down, const void* shared_w_gate_up,
+                            const void* shared_w_down, void* out, void* shared_out,
+                            float* topk_weights_out, int32_t* topk_ids_out, void* stream) {
+  const int st = check_ffn_cfg(cfg);
+  if (st) return st;
+  if (ffn_ws_layout(*cfg).total > MOE_FFN_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_LAUNCH;
+  return moe_ffn_forward(cfg, hidden, logits, correction_bias, expert_ids, w_gate_up, w_down,
+                         b_gate_up, b_down, shared_w_gate_up, shared_w_down, out, shared_out,
+                         topk_weights_out, topk_ids_out, ws, MOE_FFN_NOALLOC_SCRATCH_BYTES,
+                         stream);
 }
 
 }  // extern "C"

@@ -24,7 +24,7 @@ def header_functions():
 
 def test_library_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     assert set(names) == set(B.SYMBOLS)
     L = B.lib()
     for n in names:
@@ -286,3 +286,15 @@ def test_probe_library_exports_its_symbols():
     assert L.moe_probe_stream_read(None, 1024, None, 1, None) == 1
     assert L.moe_probe_stream_read(16, 1000, 16, 1, None) == 1
     assert L.moe_probe_mfma_bf16(0, 16, 1, None) == 1
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_scratch():
+    """moe_ffn_forward_noalloc checks the workspace moe_ffn_workspace_size would need
+    against its fixed scratch on the host and refuses before touching the GPU."""
+    L = B.lib()
+    big = B.ffn_cfg(I.CONFIGS["qwen3_bf16"])  # about 190 MiB of workspace
+    assert L.moe_ffn_workspace_size(ctypes.byref(big)) > B.NOALLOC_SCRATCH_BYTES
+    args = [None] * 14 + [None]
+    assert L.moe_ffn_forward_noalloc(ctypes.byref(big), *args) == B.MOE_ERR_WORKSPACE
+    bad = B.ffn_cfg(I.CONFIGS["qwen3_bf16"].with_(T=-1))
+    assert L.moe_ffn_forward_noalloc(ctypes.byref(bad), *args) == B.MOE_ERR_INVALID_ARG
