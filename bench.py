@@ -110,7 +110,7 @@ def host_description() -> dict:
 def measured_ceilings(reps: int = 5) -> dict:
     """The device's attainable streaming-read bandwidth and dense bf16 MFMA rate, from the
     probes of libmoe_probes.so (include/moe_probes.h), timed with HIP events on the
-    current stream: a 4 GiB read with 16-byte loads, and four independent
+    current stream: a 4 GiB read with non-temporal 16-byte loads, and four independent
     v_mfma_f32_32x32x16_bf16 chains per wave at two waves per SIMD. Best of `reps`."""
     path = os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "libmoe_probes.so")
     L = ctypes.CDLL(path)
@@ -123,7 +123,7 @@ def measured_ceilings(reps: int = 5) -> dict:
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
-    grid = cus * 16
+    grid = cus * 2
     sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
 
     def read():
@@ -144,7 +144,8 @@ def measured_ceilings(reps: int = 5) -> dict:
     flops = mgrid * 4 * iters * 4 * 2 * 32 * 32 * 16
     return {"hbm_read_GBs": round(nbytes / (t_read * 1e-3) / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
-            "source": "probes/ceilings.hip (4 GiB streaming read; bf16 32x32x16 MFMA loop)"}
+            "source": "probes/ceilings.hip (4 GiB non-temporal streaming read; bf16 32x32x16 "
+                      "MFMA loop)"}
 
 
 def log(*a):
@@ -183,6 +184,32 @@ def layer_algorithmic(cfg, n_experts: int):
         by += 3 * cfg.F_s * cfg.H * s + cfg.T * cfg.H * s + 2 * cfg.T * cfg.F_s * s
         fl += 6 * cfg.T * cfg.H * cfg.F_s
     return by, fl
+
+
+def host_layer_inputs(cfg):
+    """Counter runs of a layer workload: logits, bias, hidden and the shared expert are
+    generated on the host (the same values as on the device), and expert 0's weights,
+    generated on the host, are copied to every expert. The profiled process then launches
+    no generator kernels; the routing, and so every kernel's byte traffic, is the
+    workload's own (the GEMMs' traffic does not depend on the weight values)."""
+    d = {k: v.to("cuda") for k, v in I.make_router_inputs(cfg, device="cpu").items()}
+    dt = cfg.torch_dtype
+    d["hidden"] = I.normal((cfg.T, cfg.H), cfg.x_std, seed=0, stream=I.STREAMS["hidden"],
+                           dtype=dt).to("cuda")
+    for name, shape in (("w_gate_up", (2 * cfg.F, cfg.H)), ("w_down", (cfg.H, cfg.F))):
+        one = I.normal((1,) + shape, cfg.w_std, seed=0, stream=I.STREAMS[name], dtype=dt)
+        d[name] = one.to("cuda").expand(cfg.E, *shape).contiguous()
+    if cfg.bias_std is not None:
+        for name, n in (("b_gate_up", 2 * cfg.F), ("b_down", cfg.H)):
+            d[name] = I.normal((cfg.E, n), cfg.bias_std, seed=0, stream=I.STREAMS[name],
+                               dtype=dt).to("cuda")
+    if cfg.F_s:
+        d["shared_w_gate_up"] = I.normal((2 * cfg.F_s, cfg.H), cfg.w_std, seed=0,
+                                         stream=I.STREAMS["shared_w_gate_up"],
+                                         dtype=dt).to("cuda")
+        d["shared_w_down"] = I.normal((cfg.H, cfg.F_s), cfg.w_std, seed=0,
+                                      stream=I.STREAMS["shared_w_down"], dtype=dt).to("cuda")
+    return d
 
 
 def run_layer(cfg, d, fcfg, ws, out, shared_out):
@@ -617,7 +644,8 @@ def main(argv=None):
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured stream-read and MFMA-loop ceilings")
     ap.add_argument("--host-inputs", action="store_true",
-                    help="FP8 workloads: replicate one host-generated expert (counter runs)")
+                    help="FP8 and layer workloads: host-generated inputs, one expert's weights "
+                         "copied to every expert (counter runs; the traffic is unchanged)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the path is built and measured on a single "
@@ -644,8 +672,8 @@ def main(argv=None):
         router_line(cfg, args)
         return
     torch.cuda.set_device(0)
-    log(f"[bench] {cfg.name}: generating inputs")
-    d = I.make_inputs(cfg, device="cuda")
+    log(f"[bench] {cfg.name}: generating inputs" + (" on the host" if args.host_inputs else ""))
+    d = host_layer_inputs(cfg) if args.host_inputs else I.make_inputs(cfg, device="cuda")
     fcfg = B.ffn_cfg(cfg, args.backend)
     backend = {1: "staged", 2: "indexed"}[B.moe_ffn_backend(fcfg, cfg.bias_std is not None)]
     ws = torch.empty(B.moe_ffn_workspace_size(fcfg), dtype=torch.uint8, device="cuda")

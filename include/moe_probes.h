@@ -17,8 +17,9 @@
 extern "C" {
 #endif
 
-/* Reads `bytes` bytes of `src` (16-byte aligned, bytes a multiple of 16) once, with
- * 16-byte loads by `grid` workgroups of 256 threads in a grid-stride loop. `sink` holds
+/* Reads `bytes` bytes of `src` (16-byte aligned, bytes a multiple of 16) once with
+ * non-temporal 16-byte loads, `grid` workgroups of 256 threads each reading one
+ * contiguous 1/grid of the buffer, eight loads in flight per thread. `sink` holds
  * `grid` ints; a workgroup writes its entry only when its checksum of the data equals
  * a value ordinary data does not produce, so the loads cannot be optimised away and
  * nothing is written in practice. Returns hipErrorInvalidValue on bad sizes. */

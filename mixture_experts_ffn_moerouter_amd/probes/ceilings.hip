@@ -15,19 +15,25 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 constexpr int kThreads = 256;
 constexpr int kMagic = 0x5a5a1234;  // a checksum ordinary probe data does not produce
 
-// Each thread reads 16-byte vectors i, i + S, i + 2S, ... (S = grid threads), four loads
-// in flight per iteration, and folds them into a checksum.
+// Workgroup b reads the contiguous run of 16-byte vectors [b per, (b + 1) per); each thread
+// keeps eight non-temporal loads in flight (lines are streamed once, so they are fetched
+// with the hint that they will not be reused) and folds them into a checksum.
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const i32x4* __restrict__ src,
-                                                               int64_t n, int32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+                                                               int64_t n, int64_t per,
+                                                               int32_t* sink) {
+  constexpr int U = 8;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n ? lo + per : n;
   i32x4 acc = {0, 0, 0, 0};
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const i32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride],
-                d = src[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+  int64_t i = lo + threadIdx.x;
+  for (; i + (U - 1) * kThreads < hi; i += U * kThreads) {
+    i32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + i + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u];
   }
-  for (; i < n; i += stride) acc ^= src[i];
+  for (; i < hi; i += kThreads) acc ^= src[i];
   const int v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   if (v == kMagic) sink[blockIdx.x] = v;
 }
@@ -61,8 +67,9 @@ int moe_probe_stream_read(const void* src, int64_t bytes, int32_t* sink, int32_t
                           void* stream) {
   if (!src || !sink || grid < 1 || bytes < 16 || bytes % 16 || ((uintptr_t)src & 15))
     return (int)hipErrorInvalidValue;
-  stream_read_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>((const i32x4*)src,
-                                                                  bytes / 16, sink);
+  const int64_t n = bytes / 16, per = (n + grid - 1) / grid;
+  stream_read_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>((const i32x4*)src, n, per,
+                                                                  sink);
   return (int)hipGetLastError();
 }
 
