@@ -45,10 +45,14 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # time, and a different source reports null.
 TRAFFIC = {
     # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
-    # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE).
-    # gate_up: 500898.3 + 50120.7 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1077137488,
-                   "gemm_src": "7cf169e11cc66834da1d9f851ef669ed1f1512760774557ff5b25c9674364282"},
+    # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
+    # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
+    # routed gate_up: 8565158.8 + 147783.6 KiB
+    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17692334456,
+                  "gemm_src": "31cbfe87260944b50b30b0e109841ca39a4c8b7a5959ef26be510b8197033c95"},
+    # routed gate_up: 485878.5 + 49936.1 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1046188599,
+                   "gemm_src": "31cbfe87260944b50b30b0e109841ca39a4c8b7a5959ef26be510b8197033c95"},
     # FP8 (a 1 GiB copy read 524301.2 KiB of FETCH_SIZE): 4512238.0 + 263745.7 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9510906364,
                          "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
