@@ -218,6 +218,9 @@ int moe_permute(const int32_t* topk_ids, int64_t T, int64_t K, int64_t E,
  * for bf16/f16, M*H*2 and 2F*H*2 below 2^31 bytes (32-bit offsets; a gathered source
  * must also stay below 2^31 bytes). INVALID_ARG for gelu_and_mul with INTERLEAVED rows.
  * Errors: INVALID_ARG, UNSUPPORTED, OVERLAP (out vs a, weights, bias, offsets, a_rows).
+ * With a gather, the rows read are named by a_rows on the device, which the host does
+ * not read: OVERLAP covers a's first row only, and out must not overlap any gathered row
+ * (a precondition, like the device metadata's ranges).
  * ------------------------------------------------------------------------------- */
 int moe_grouped_gemm_swiglu(const void* a, const int32_t* a_rows, int32_t a_rows_div,
                             int64_t M, int64_t H, const void* w_gate_up,

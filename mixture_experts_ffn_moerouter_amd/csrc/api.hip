@@ -302,7 +302,9 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   if (ws_need && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
   Range ins[] = {{b, (size_t)E * Nw * Kd * s}, {bias, bias ? (size_t)E * Nw * s : 0},
                  {offsets, meta_bytes}, {a_rows, a_rows ? (size_t)M * 4 : 0},
-                 {a, a_rows ? 1 : (size_t)M * Kd * s}};
+                 // gathered: the source rows are named by device data, not read here;
+                 // only the first row is known (overlap with the rest is a precondition)
+                 {a, a_rows ? (size_t)Kd * s : (size_t)M * Kd * s}};
   Range outs[] = {{out, (size_t)M * Nout * dt_size(out_dt)}, {workspace, ws_need}};
   if (any_overlap(outs, 2, ins, 5)) return MOE_ERR_OVERLAP;
   if (M == 0) return MOE_OK;

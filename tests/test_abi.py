@@ -125,6 +125,10 @@ def test_gemm_combine_permute_argument_errors():
                                    FAKE + (1 << 24), 1, ctypes.byref(act), FAKE + (1 << 20) + 64,
                                    None)
     assert st == B.MOE_ERR_OVERLAP
+    # gathered A: out over the source's first row (past its first byte) is refused
+    st = L.moe_grouped_gemm(FAKE, FAKE + (1 << 26), 8, 16, 64, FAKE + (1 << 20), None, 2, 32,
+                            FAKE + (1 << 24), 1, 1, FAKE + 64, None)
+    assert st == B.MOE_ERR_OVERLAP
     # bf16 rows must be a multiple of 8 elements
     st = L.moe_grouped_gemm(FAKE, None, 1, 16, 60, FAKE + (1 << 20), None, 2, 32,
                             FAKE + (1 << 24), 1, 1, FAKE + (1 << 28), None)
