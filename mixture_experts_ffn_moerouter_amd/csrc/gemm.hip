@@ -237,8 +237,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
-    // The K loop, compiled for kNI and for kNI - 2 live 16-row blocks of the wave (blocks
-    // past the live ones multiply zeros and are not stored).
+    // The K loop, compiled for each count of live 16-row blocks of the wave (1 .. kNI).
     auto main_loop = [&](auto ni_c) {
       constexpr int NI = decltype(ni_c)::value;
       constexpr int NB = NI * 8;  // MFMAs per step
@@ -284,8 +283,16 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         }
       }
     };
-    if (nbw > kNI - 2) main_loop(std::integral_constant<int, kNI>{});
-    else main_loop(std::integral_constant<int, kNI - 2>{});
+    // One instance per count of live blocks (dead blocks would only multiply zeros). Every
+    // wave runs exactly one of them, a wave without live rows the one-block instance: its
+    // transfers and barriers are the other waves' too.
+    const int ni = nbw < 1 ? 1 : (nbw > kNI ? kNI : nbw);
+    static_assert(kNI == 4 || kNI == 5, "instances below");
+    if (ni == kNI) main_loop(std::integral_constant<int, kNI>{});
+    else if (ni == kNI - 1) main_loop(std::integral_constant<int, kNI - 1>{});
+    else if (ni == kNI - 2) main_loop(std::integral_constant<int, kNI - 2>{});
+    else if (kNI == 5 && ni == 2) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
     gs += nk;
 
     // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
