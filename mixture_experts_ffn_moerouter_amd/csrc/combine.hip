@@ -8,8 +8,8 @@
 //
 // One workgroup per token and chunk of kChunk hidden elements (several per token when H is
 // large, so small batches still spread over the chip); each thread owns 8 consecutive
-// elements (16-byte loads of 16-bit rows), sums its K rows in float32 in k order and
-// writes once.
+// elements (16-byte loads of 16-bit rows, non-temporal: each expert output is read once),
+// sums its K rows in float32 in k order and writes once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -26,7 +26,7 @@ __device__ __forceinline__ void load8(const void* p, float* v) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
   } else {
-    i32x4 q = *(const i32x4*)p;
+    i32x4 q = __builtin_nontemporal_load((const i32x4*)p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = h16_to_f32<YDT>((uint16_t)((uint32_t)q[i] & 0xffffu));

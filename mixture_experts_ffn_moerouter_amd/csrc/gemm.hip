@@ -489,11 +489,24 @@ hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
 // contraction runs with two.
 // 160-row tiles need three stages and the tile map of E experts in LDS (E up to 335);
 // otherwise 128-row tiles (E up to 1024).
+// A single expert owning every row (a dense GEMM, e.g. the shared expert) has a tile count
+// the host knows: there the tile height with fewer rounds of tiles over the CUs wins, each
+// round weighted by its tile's transfer bytes per step (tile rows + 256).
 template <bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG = 0>
 hipError_t launch_h16_act(const GemmArgs& g, hipStream_t s) {
   if (g.Kd <= kBK) return launch_h16_ns<2, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
-  if (3 * stage_bytes(160) + map_bytes(g.E) + kStaticLds <= kLds)
-    return launch_h16_ns<3, 160, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  bool tall = 3 * stage_bytes(160) + map_bytes(g.E) + kStaticLds <= kLds;
+  if (tall && g.seg_mode == kSegOffsets && !g.offsets) {
+    const int64_t nt = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
+    const int64_t cus = cu_count() / kXcd * kXcd;
+    auto cost = [&](int bm) {
+      const int64_t rows = ((int64_t)g.M + bm - 1) / bm, tpt = (g.M + rows - 1) / rows;
+      const int64_t h = (tpt + 31) / 32 * 32;  // rows_per_tile
+      return ((rows * nt + cus - 1) / cus) * (h + kBNW);
+    };
+    tall = cost(160) <= cost(128);
+  }
+  if (tall) return launch_h16_ns<3, 160, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
   return launch_h16_ns<3, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
 }
 static_assert(3 * stage_bytes(128) + map_bytes(1024) + kStaticLds <= kLds, "LDS");
