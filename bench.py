@@ -91,9 +91,24 @@ def copy_calibration():
           flush=True)
 
 
-def host_description() -> dict:
-    """CPU threads the oracle's BLAS uses (what the baseline actually ran on), the CPUs
-    this process may run on, and the CPU model."""
+def oracle_threads() -> int:
+    """Threads the C oracle runs on: the CPUs this process may use, capped by
+    OMP_NUM_THREADS when that is set (a host's share of cores for one GPU)."""
+    try:
+        cpus = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cpus = os.cpu_count() or 1
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(cpus, cap) if cap > 0 else cpus)
+
+
+def host_description(cores: int = 0) -> dict:
+    """The CPU threads the baseline actually ran on (`cores`: the C oracle's worker
+    threads, or the numpy oracle's BLAS threads when not given), the CPUs this process
+    may run on, and the CPU model."""
     try:
         cpus = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
@@ -107,7 +122,7 @@ def host_description() -> dict:
                     break
     except OSError:  # pragma: no cover
         pass
-    return {"cores": _blas_threads(), "host_cpus": cpus, "cpu_model": model,
+    return {"cores": cores or _blas_threads(), "host_cpus": cpus, "cpu_model": model,
             "os_cpu_count": os.cpu_count()}
 
 
@@ -353,22 +368,25 @@ def router_line(cfg, args):
                      "algorithmic_bytes": k_bytes},
     }
     if not args.no_cpu_baseline:
-        import oracle.moe_oracle as O
-        logits = d["logits"].float().cpu().numpy().astype(np.float64)
+        from oracle.c_oracle import load
+        Cx = load(1)  # the C router takes one row after another on one thread
+        logits = d["logits"].cpu()
         bias = None if d.get("correction_bias") is None else \
             d["correction_bias"].cpu().numpy().astype(np.float64)
+        rp = cfg.router_probs_dtype if cfg.local_expert_count else None
         done, total = 0, 0.0
         n = min(cfg.T, 256)
         while total < args.cpu_budget / 4:
             t1 = time.perf_counter()
-            O.route(logits[:n], cfg.K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG,
-                    bias)
+            Cx.route(logits[:n], cfg.K, cfg.scoring, cfg.renormalize, cfg.rsf, cfg.G, cfg.TG,
+                     bias, None, cfg.local_expert_start, cfg.local_expert_count or None, rp)
             total += time.perf_counter() - t1
             done += n
         line["cpu_baseline"] = {"value": done / total, "unit": "tokens/s",
-                                **host_description(), "kind": "oracle",
+                                **host_description(1), "kind": "oracle",
                                 "sample": f"first {n} of {cfg.T} tokens, repeated "
-                                          f"({done} routed), float64 numpy oracle, {total:.1f} s"}
+                                          f"({done} routed), float64 C oracle "
+                                          f"(oracle/moe_ref.c), one thread, {total:.1f} s"}
     print(json.dumps(line), flush=True)
 
 
@@ -415,18 +433,20 @@ def swiglu_line(cfg, args):
                      "kernel_ms": round(k_ms, 5), "algorithmic_bytes": k_bytes},
     }
     if not args.no_cpu_baseline:
-        import oracle.moe_oracle as O
+        from oracle.c_oracle import load
+        Cx = load(1)  # the C activation runs element after element on one thread
         x = d["gate"][:512].float().cpu().numpy().astype(np.float64)
         done, total = 0, 0.0
         while total < args.cpu_budget / 4:
             t1 = time.perf_counter()
-            O.swiglu_op(x, None, cfg.alpha, cfg.beta, cfg.limit, cfg.fusion, cfg.dtype)
+            Cx.swiglu_op(x, None, cfg.alpha, cfg.beta, cfg.limit, cfg.fusion, cfg.dtype)
             total += time.perf_counter() - t1
             done += x.shape[0]
         line["cpu_baseline"] = {"value": done / total, "unit": "rows/s",
-                                **host_description(), "kind": "oracle",
+                                **host_description(1), "kind": "oracle",
                                 "sample": f"first 512 of {cfg.rows} rows, repeated ({done} "
-                                          f"rows), float64 numpy oracle, {total:.1f} s"}
+                                          f"rows), float64 C oracle (oracle/moe_ref.c), one "
+                                          f"thread, {total:.1f} s"}
     print(json.dumps(line), flush=True)
 
 
@@ -580,55 +600,63 @@ def fp8_line(cfg, args):
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        import oracle.moe_oracle as O
+        from oracle.c_oracle import load
+        threads = oracle_threads()
+        Cx = load(threads)
         done, total, g = 0, 0.0, 0
         while total < args.cpu_budget / 2 and g < cfg.E:
             sub = {k: v[g:g + 1].cpu().numpy() for k, v in d.items() if k != "counts"}
             t1 = time.perf_counter()
-            O.grouped_gemm_fp8_masked(sub["a"], sub["a_scale"], sub["b"], sub["b_scale"],
-                                      counts[g:g + 1])
+            Cx.grouped_gemm_fp8_masked(sub["a"].view(np.uint8), sub["a_scale"],
+                                       sub["b"].view(np.uint8), sub["b_scale"], counts[g:g + 1])
             total += time.perf_counter() - t1
             done += int(counts[g])
             g += 1
         line["cpu_baseline"] = {
-            "value": done / 8.0 / total, "unit": "tokens/s", **host_description(),
+            "value": done / 8.0 / total, "unit": "tokens/s", **host_description(threads),
             "kind": "oracle",
             "sample": f"experts 0..{g - 1} of {cfg.E} ({done} of {rows} valid rows), float64 "
-                      f"numpy oracle, {total:.1f} s"}
+                      f"C oracle (oracle/moe_ref.c) on {threads} threads, {total:.1f} s"}
     print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(cfg, d, budget_s: float):
-    """The CPU oracle, as it stands, on the first n tokens of the same workload."""
-    import oracle.moe_oracle as O
-    host = {k: (v.float().cpu().numpy() if v.is_floating_point() else v.cpu().numpy())
-            for k, v in d.items()}
+    """The C oracle (oracle/moe_ref.c), as it stands, on the first n tokens of the same
+    workload: inputs in their storage formats on the host, one token per worker thread at
+    a time, on every CPU this process may use."""
+    from oracle.c_oracle import load
+    threads = oracle_threads()
+    Cx = load(threads)
+    host = {k: v.cpu() for k, v in d.items()}
+    bias = host.get("correction_bias")
     kw = dict(top_k=cfg.K, scoring=cfg.scoring, renormalize=cfg.renormalize,
               routed_scaling_factor=cfg.rsf, num_expert_group=cfg.G, topk_group=cfg.TG,
-              act=cfg.act, dtype=cfg.dtype, correction_bias=host.get("correction_bias"),
-              expert_ids=host.get("expert_ids"), b_gate_up=host.get("b_gate_up"),
-              b_down=host.get("b_down"), shared_w_gate_up=host.get("shared_w_gate_up"),
+              act=cfg.act, dtype=cfg.dtype,
+              correction_bias=None if bias is None else bias.double().numpy(),
+              b_gate_up=host.get("b_gate_up"), b_down=host.get("b_down"),
+              shared_w_gate_up=host.get("shared_w_gate_up"),
               shared_w_down=host.get("shared_w_down"))
-    n = min(cfg.T, 64)
-    while True:  # grow the sample until one pass takes a third of the budget
+    ids = host.get("expert_ids")
+
+    def run(n):
         t0 = time.perf_counter()
-        O.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
-                          host["w_down"], **kw)
-        dt = time.perf_counter() - t0
+        Cx.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
+                           host["w_down"], expert_ids=None if ids is None else ids[:n], **kw)
+        return time.perf_counter() - t0
+    n = min(cfg.T, threads)
+    while True:  # grow the sample until one pass takes a third of the budget
+        dt = run(n)
         if dt >= budget_s / 3 or n >= cfg.T:
             break
         n = min(cfg.T, n * 4)
     passes, total = 1, dt
     while total < budget_s / 2:  # whole workload is quick: repeat it to about 10 s
-        t0 = time.perf_counter()
-        O.moe_ffn_forward(host["hidden"][:n], host["logits"][:n], host["w_gate_up"],
-                          host["w_down"], **kw)
-        total += time.perf_counter() - t0
+        total += run(n)
         passes += 1
-    return {"value": n * passes / total, "unit": "tokens/s", **host_description(),
+    return {"value": n * passes / total, "unit": "tokens/s", **host_description(threads),
             "kind": "oracle",
             "sample": f"first {n} of {cfg.T} tokens of the same workload, {passes} pass(es), "
-                      f"float64 numpy oracle (BLAS matmuls on 'cores' threads), "
+                      f"float64 C oracle (oracle/moe_ref.c) on {threads} threads, "
                       f"{total:.1f} s wall"}
 
 

@@ -352,6 +352,35 @@ def pin_layout_and_bias_identities():
     assert np.allclose(y5, y6 + bd[None, :], rtol=1e-13)
 
 
+def pin_activation_rounding_point():
+    """The gated activation is stored in the operand dtype before the down projection.
+    One-hot tokens make h a weight column exactly, a down weight of 3 I makes y = 3 a
+    exactly, and top-1 routing over one expert gives weight 1; so the layer output is
+    bf16(3 bf16(act(h))), which differs from bf16(3 act(h)) on this fixture."""
+    r = _rng(31)
+    n = 16
+    x = np.eye(n)
+    wgu = torch.from_numpy(r.standard_normal((1, 2 * n, n))).to(torch.bfloat16)
+    wgu = wgu.to(torch.float64).numpy()
+    wd = (3.0 * np.eye(n))[None]
+    out = O.moe_ffn_forward(x, np.zeros((n, 1)), wgu, wd, top_k=1, renormalize=True,
+                            dtype="bf16")["out"]
+    g, u = wgu[0, :n].T, wgu[0, n:].T             # h[t] = column t of the weight
+    act = g / (1.0 + np.exp(-g)) * u
+
+    def bf(v):
+        # torch rounds through float32; that equals one rounding unless the float32 value
+        # is a bfloat16 midpoint while v itself is not (checked here)
+        v = np.asarray(v, np.float64)
+        v32 = v.astype(np.float32)
+        mid = (v32.view(np.uint32) & 0xFFFF) == 0x8000
+        assert not np.any(mid & (v32.astype(np.float64) != v))
+        return torch.from_numpy(v32).to(torch.bfloat16).to(torch.float64).numpy()
+    want = bf(3.0 * bf(act))
+    assert not np.array_equal(want, bf(3.0 * act))  # the fixture tells the two apart
+    assert np.array_equal(out, want)
+
+
 # ------------------------------------------------------------------- stages
 def pin_grouped_gemm_bruteforce():
     r = _rng(9)

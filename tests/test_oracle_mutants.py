@@ -58,6 +58,11 @@ def _combine_transposed(y, topk_weights, route_pos, scale=1.0, out_dtype="f32"):
     return O.round_to(scale * out, out_dtype)
 
 
+def _expert_mlp_unrounded_act(x, w_gate_up, w_down, b_gate_up=None, b_down=None,
+                              act="silu_and_mul", act_dtype="f32"):
+    return _orig_expert_mlp(x, w_gate_up, w_down, b_gate_up, b_down, act, "f64")
+
+
 def _expert_mlp_no_down_bias(x, w_gate_up, w_down, b_gate_up=None, b_down=None,
                              act="silu_and_mul", act_dtype="f32"):
     return _orig_expert_mlp(x, w_gate_up, w_down, b_gate_up, None, act, act_dtype)
@@ -258,6 +263,7 @@ MUTANTS = {
     "renormalized over all experts": ("routing_weights", _weights_biased),
     "combine reads route_pos transposed": ("combine", _combine_transposed),
     "down bias dropped": ("expert_mlp", _expert_mlp_no_down_bias),
+    "activation not stored in the operand dtype": ("expert_mlp", _expert_mlp_unrounded_act),
     "rounding truncates": ("round_to", _round_truncate),
     "sqrt_softplus drops a term": ("scores", _scores_sqrt_softplus_wrong),
     "biased group score is the max": ("select_experts", _group_max_with_bias),
