@@ -46,51 +46,34 @@ __device__ __forceinline__ void store8f(void* base, int64_t i, const float* v) {
   }
 }
 
-#ifndef SWIGLU_UNROLL
-#define SWIGLU_UNROLL 1
-#endif
-constexpr int kUnroll = SWIGLU_UNROLL;  // items whose loads are in flight together
-
 // MODE 0: gate and up separate [rows, F]; 1: fused stacked [rows, 2F]; 2: fused interleaved.
+// One item is eight consecutive outputs of a row.
 template <int DT, int MODE>
 __global__ __launch_bounds__(256) void swiglu_vec_kernel(SwigluArgs a) {
   const int F = a.F, per_row = F / 8;
   const int64_t items = a.rows * per_row;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it0 < items;
-       it0 += stride * kUnroll) {
-    float g[kUnroll][8], u[kUnroll][8];
-    int64_t orow[kUnroll];
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += stride) {
+    const int64_t r = it / per_row;
+    const int j = (int)(it - r * per_row) * 8;
+    float g[8], u[8];
+    if constexpr (MODE == 0) {
+      load8f<DT>(a.gate, r * F + j, g);
+      load8f<DT>(a.up, r * F + j, u);
+    } else if constexpr (MODE == 1) {
+      load8f<DT>(a.gate, r * 2 * F + j, g);
+      load8f<DT>(a.gate, r * 2 * F + F + j, u);
+    } else {
+      float p[16];
+      load8f<DT>(a.gate, r * 2 * F + 2 * j, p);
+      load8f<DT>(a.gate, r * 2 * F + 2 * j + 8, p + 8);
 #pragma unroll
-    for (int q = 0; q < kUnroll; ++q) {
-      // items past the end repeat the last one (loaded, not stored)
-      const int64_t it = min(it0 + q * stride, items - 1);
-      const int64_t r = it / per_row;
-      const int j = (int)(it - r * per_row) * 8;
-      orow[q] = r * F + j;
-      if constexpr (MODE == 0) {
-        load8f<DT>(a.gate, r * F + j, g[q]);
-        load8f<DT>(a.up, r * F + j, u[q]);
-      } else if constexpr (MODE == 1) {
-        load8f<DT>(a.gate, r * 2 * F + j, g[q]);
-        load8f<DT>(a.gate, r * 2 * F + F + j, u[q]);
-      } else {
-        float p[16];
-        load8f<DT>(a.gate, r * 2 * F + 2 * j, p);
-        load8f<DT>(a.gate, r * 2 * F + 2 * j + 8, p + 8);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) { g[q][k] = p[2 * k]; u[q][k] = p[2 * k + 1]; }
-      }
+      for (int k = 0; k < 8; ++k) { g[k] = p[2 * k]; u[k] = p[2 * k + 1]; }
     }
+    float o[8];
 #pragma unroll
-    for (int q = 0; q < kUnroll; ++q) {
-      if (it0 + q * stride < items) {
-        float o[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k] = swiglu_f(g[q][k], u[q][k], a.alpha, a.beta, a.limit);
-        store8f<DT>(a.out, orow[q], o);
-      }
-    }
+    for (int k = 0; k < 8; ++k) o[k] = swiglu_f(g[k], u[k], a.alpha, a.beta, a.limit);
+    store8f<DT>(a.out, r * F + j, o);
   }
 }
 
