@@ -47,18 +47,18 @@ TRAFFIC = {
     # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
     # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
     # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
-    # routed gate_up: 8565158.8 + 147783.6 KiB
-    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17692334456,
-                  "gemm_src": "31cbfe87260944b50b30b0e109841ca39a4c8b7a5959ef26be510b8197033c95"},
-    # routed gate_up: 485878.5 + 49936.1 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1046188599,
-                   "gemm_src": "31cbfe87260944b50b30b0e109841ca39a4c8b7a5959ef26be510b8197033c95"},
-    # FP8 (a 1 GiB copy read 524301.2 KiB of FETCH_SIZE): 4512238.0 + 263745.7 KiB
-    "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9510906364,
-                         "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
-    # 1909139.3 + 463106.7 KiB
-    "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4384040110,
-                      "gemm_src": "cb3db2542fd1563f85121001220cc70f149824e04de59fa43f1c52974ff42cc9"},
+    # routed gate_up: 8391816.1 + 146743.5 KiB
+    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17336270891,
+                  "gemm_src": "81f1977ac6e19ff23ef6918619d515e241f096d9dc0ed386aca69fba88739fc1"},
+    # routed gate_up: 513067.2 + 50809.6 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1102764226,
+                   "gemm_src": "81f1977ac6e19ff23ef6918619d515e241f096d9dc0ed386aca69fba88739fc1"},
+    # FP8, profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
+    "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9308609010,
+                         "gemm_src": "b9cb208a3af70110206db8b73178454194983587a3260105600d56e2ab4f470d"},
+    # 1909742.6 + 462315.2 KiB
+    "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4384464964,
+                      "gemm_src": "b9cb208a3af70110206db8b73178454194983587a3260105600d56e2ab4f470d"},
 }
 
 
