@@ -37,6 +37,11 @@
 // v_mfma_f32_16x16x32 per step, weights as the first operand, so a lane's four results
 // are four consecutive outputs of one token row: one 8-byte store (16 in float32).
 //
+// Cache policy. A tile of an expert that has one row tile reads each of its weight lines
+// once, so that tile's weight transfers are non-temporal; an expert with more row tiles
+// keeps its weight lines in the L2 for the later ones. Token rows (read by every n-tile)
+// keep the default policy.
+//
 // Work. The grid is one workgroup per CU, each walking a list of tiles: the stage ring
 // runs across tile boundaries, so the next tile's first steps load during the current
 // tile's last steps and its epilogue. An expert with M_e rows gets ceil(M_e / 128) row
@@ -70,8 +75,9 @@ constexpr int stage_bytes(int bm) { return (bm + kBNW) * 128; }
 constexpr int map_bytes(int E) { return 3 * (E + 1) * (int)sizeof(int); }
 constexpr int kStaticLds = 64;          // s_tmp and alignment
 
+template <int AUX = 0>
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, AUX);
 }
 
 // 16 x 16 x 32 MFMA on eight 16-bit elements per lane: DT 1 bfloat16, 2 float16.
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   tile(0, te, tnt, tm0, tm1);
   offsets(te, tnt, tm0, tm1, aC, bC, rbC);
   // transfer p of step kk of this tile (nxt false) or the next into stage st
-  auto piece = [&](int stage, int kk, bool nxt, int p) {
+  auto piece = [&](int stage, int kk, bool nxt, int p, auto aux_c) {
     uint8_t* st = smem + stage * kStage;
     const int k0 = kk * kBK;
     const bool in = k0 + kel < Kd;
@@ -194,8 +200,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
       dma16(ra, st + apiece(p) * 1024, in ? o + kbyte : kOOB);
     } else {
       const uint32_t o = nxt ? bN[p - kPA] : bC[p - kPA];
-      dma16(nxt ? rbN : rbC, st + BM * 128 + (kPB * wave + p - kPA) * 1024,
-            in ? o + kbyte : kOOB);
+      dma16<decltype(aux_c)::value>(nxt ? rbN : rbC,
+                                    st + BM * 128 + (kPB * wave + p - kPA) * 1024,
+                                    in ? o + kbyte : kOOB);
     }
   };
 
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
 #pragma unroll
   for (int q = 0; q < LA; ++q)
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p) piece(q, q, false, p);
+    for (int p = 0; p < kPieces; ++p) piece(q, q, false, p, std::integral_constant<int, 0>{});
 
   const uint16_t* bias = (const uint16_t*)g.bias;
   const bool aligned = ((uintptr_t)g.out & 15) == 0;
@@ -238,7 +245,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
     // The K loop, compiled for each count of live 16-row blocks of the wave (1 .. kNI).
-    auto main_loop = [&](auto ni_c) {
+    auto main_loop = [&](auto ni_c, auto aux_c) {
       constexpr int NI = decltype(ni_c)::value;
       constexpr int NB = NI * 8;  // MFMAs per step
       constexpr int EVERY = NB / kPieces;
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         for (int t = 0; t < NB; ++t) {
           const int c = t / (NI * 4), u = t % (NI * 4), i = u / 4, j = u % 4;
           acc[i][j] = mfma16<DT>(fb[j][c], fa[i][c], acc[i][j]);
-          if (t % EVERY == EVERY - 1 && t / EVERY < kPieces) piece(s2, kk, nxt, t / EVERY);
+          if (t % EVERY == EVERY - 1 && t / EVERY < kPieces) piece(s2, kk, nxt, t / EVERY, aux_c);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -287,12 +294,18 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     // wave runs exactly one of them, a wave without live rows the one-block instance: its
     // transfers and barriers are the other waves' too.
     const int ni = nbw < 1 ? 1 : (nbw > kNI ? kNI : nbw);
-    static_assert(kNI == 4 || kNI == 5, "instances below");
-    if (ni == kNI) main_loop(std::integral_constant<int, kNI>{});
-    else if (ni == kNI - 1) main_loop(std::integral_constant<int, kNI - 1>{});
-    else if (ni == kNI - 2) main_loop(std::integral_constant<int, kNI - 2>{});
-    else if (kNI == 5 && ni == 2) main_loop(std::integral_constant<int, 2>{});
-    else main_loop(std::integral_constant<int, 1>{});
+    // an expert with one row tile reads each weight line once: non-temporal weight loads
+    const bool once = __builtin_amdgcn_readfirstlane(s_pre[e + 1] - s_pre[e]) == 1;
+    auto run = [&](auto aux_c) {
+      static_assert(kNI == 4 || kNI == 5, "instances below");
+      if (ni == kNI) main_loop(std::integral_constant<int, kNI>{}, aux_c);
+      else if (ni == kNI - 1) main_loop(std::integral_constant<int, kNI - 1>{}, aux_c);
+      else if (ni == kNI - 2) main_loop(std::integral_constant<int, kNI - 2>{}, aux_c);
+      else if (kNI == 5 && ni == 2) main_loop(std::integral_constant<int, 2>{}, aux_c);
+      else main_loop(std::integral_constant<int, 1>{}, aux_c);
+    };
+    if (once) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 0>{});
     gs += nk;
 
     // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
