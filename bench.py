@@ -47,12 +47,12 @@ TRAFFIC = {
     # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
     # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
     # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
-    # routed gate_up: 8391816.1 + 146743.5 KiB
-    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17336270891,
-                  "gemm_src": "81f1977ac6e19ff23ef6918619d515e241f096d9dc0ed386aca69fba88739fc1"},
-    # routed gate_up: 513067.2 + 50809.6 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1102764226,
-                   "gemm_src": "81f1977ac6e19ff23ef6918619d515e241f096d9dc0ed386aca69fba88739fc1"},
+    # routed gate_up: 8363999.1 + 142723.7 KiB
+    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17275144578,
+                  "gemm_src": "031b509a0893ba26a9a9ed7e8cb0bbf4c2335950945971a2079d2fd1f9381609"},
+    # routed gate_up: 497489.8 + 50699.8 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1070747478,
+                   "gemm_src": "031b509a0893ba26a9a9ed7e8cb0bbf4c2335950945971a2079d2fd1f9381609"},
     # FP8, profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9308609010,
                          "gemm_src": "b9cb208a3af70110206db8b73178454194983587a3260105600d56e2ab4f470d"},
