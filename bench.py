@@ -18,6 +18,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,34 +41,44 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # HBM bytes of one launch of a workload's dominant GEMM, read by the FETCH_SIZE and
 # WRITE_SIZE counters (rocprofv3 --pmc, one counter per run, over this script's own
 # launches; FP8 workloads with --host-inputs) and scaled by what the same counters read for
-# a plain copy of known size (--copy-calibration). A figure belongs to the kernel source it
-# was measured on: gemm_src is the SHA-256 of that kernel's file and csrc/tile_map.h at the
-# time, and a different source reports null.
+# a plain copy of known size (--copy-calibration). A figure belongs to the kernel code it
+# was measured on: gemm_src is the SHA-256 of that kernel's file and csrc/tile_map.h with
+# their comments and blank lines removed (gemm_source_digest), and different code reports
+# null.
 TRAFFIC = {
     # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
     # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
     # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
     # routed gate_up: 8363999.1 + 142723.7 KiB
     "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17275144578,
-                  "gemm_src": "031b509a0893ba26a9a9ed7e8cb0bbf4c2335950945971a2079d2fd1f9381609"},
+                  "gemm_src": "eb43b0aa5c36ea96e3c548fff61ae39d368b773da655c89c025c22821274bcdf"},
     # routed gate_up: 497489.8 + 50699.8 KiB
     "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1070747478,
-                   "gemm_src": "031b509a0893ba26a9a9ed7e8cb0bbf4c2335950945971a2079d2fd1f9381609"},
+                   "gemm_src": "eb43b0aa5c36ea96e3c548fff61ae39d368b773da655c89c025c22821274bcdf"},
     # FP8, profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9308609010,
-                         "gemm_src": "b9cb208a3af70110206db8b73178454194983587a3260105600d56e2ab4f470d"},
+                         "gemm_src": "4be2967d76e0b9f3a697f64f0aedd7eb041a765278899cb507cc4cf3c577542e"},
     # 1909742.6 + 462315.2 KiB
     "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4384464964,
-                      "gemm_src": "b9cb208a3af70110206db8b73178454194983587a3260105600d56e2ab4f470d"},
+                      "gemm_src": "4be2967d76e0b9f3a697f64f0aedd7eb041a765278899cb507cc4cf3c577542e"},
 }
 
 
+def code_text(src: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines (the sources have
+    no string literal holding a comment marker)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*$", "", line).rstrip() for line in src.splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def gemm_source_digest(kernel: str = "gemm.hip") -> str:
-    """SHA-256 over a GEMM kernel's source and the tile-map header it includes."""
+    """SHA-256 over the code of a GEMM kernel's source and the tile-map header it includes
+    (comments do not count: editing one leaves the recorded figures valid)."""
     h = hashlib.sha256()
     for name in (kernel, "tile_map.h"):
-        with open(os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", name)) as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()
 
 

@@ -13,8 +13,10 @@
 //
 // 16-bit kernel (bfloat16 or float16 operands; only the MFMA and the conversions differ).
 //
-// Tile: 128 token rows x 256 weight rows, eight waves (2 x 4) of 64 x 64; a K step is 64
-// elements, 128 bytes of every row. For the gated activation the tile's 256 weight rows
+// Tile: BM token rows (160, or 128 where the LDS cannot hold three 160-row stages beside
+// the tile map) x 256 weight rows, eight waves (2 x 4): the two row waves take alternate
+// 16-row blocks (BM / 2 rows each), the four column waves 64 weight rows each; a K step is
+// 64 elements, 128 bytes of every row. For the gated activation the tile's 256 weight rows
 // are the gate and up rows of 128 outputs, placed so that a wave's blocks j and j + 2
 // hold the gate and the up row of the same outputs; the epilogue pairs them directly.
 //
@@ -23,8 +25,8 @@
 // instructions. Step k + NS - 1 is requested while step k is multiplied. One load
 // instruction moves 1 KB, eight rows x 128 bytes (whole cache lines): lane l lands in row
 // l / 8, 16-byte slot l % 8, and fetches the row's piece (l % 8) ^ (row % 8), so slots
-// are XOR-swizzled by row. A wave's six transfers of a step (two of token rows, four of
-// weight rows) are spread through its MFMA stream. Rows of A may be gathered (a_rows),
+// are XOR-swizzled by row. A wave's transfers of a step (BM / 64 rounded up of token rows,
+// four of weight rows) are spread through its MFMA stream. Rows of A may be gathered (a_rows),
 // so the permuted activation copy is never materialised. Out-of-range pieces (rows past
 // the tile, weight rows past N, the K tail, steps past the end) get an offset past the
 // buffer's range, so the hardware writes zeros without a branch. The compiler's
@@ -35,7 +37,9 @@
 // q + 4 of row r (both operands alike, so products pair as in the plain sum); with the
 // XOR slots these reads are free of bank conflicts. Each 16 x 16 block takes two
 // v_mfma_f32_16x16x32 per step, weights as the first operand, so a lane's four results
-// are four consecutive outputs of one token row: one 8-byte store (16 in float32).
+// are four consecutive outputs of one token row: one 8-byte store (16 in float32). The K
+// loop is compiled once per count of a wave's live 16-row blocks, so a partly filled tile
+// issues no MFMA for blocks that hold only padding.
 //
 // Cache policy. A tile of an expert that has one row tile reads each of its weight lines
 // once, so that tile's weight transfers are non-temporal; an expert with more row tiles
@@ -44,7 +48,7 @@
 //
 // Work. The grid is one workgroup per CU, each walking a list of tiles: the stage ring
 // runs across tile boundaries, so the next tile's first steps load during the current
-// tile's last steps and its epilogue. An expert with M_e rows gets ceil(M_e / 128) row
+// tile's last steps and its epilogue. An expert with M_e rows gets ceil(M_e / BM) row
 // tiles of equal height (rounded up to 32 rows); the map is built on the device from the
 // layout metadata (no host synchronisation) and kept in LDS. Logical tiles are ordered
 // expert, n-tile, row tile and each XCD takes a contiguous range, its workgroups
