@@ -3,6 +3,8 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
                     [--no-ceilings]   # default workload: dsv3_bf16
     python bench.py --copy-calibration   # a plain 1 GiB device copy, for counter scaling
+    python bench.py --compare-vendor qwen3,dsv3   # this grouped GEMM beside the vendor's
+                                                  # batched GEMM on equal-row expert shapes
 
 A step is one moe_ffn_forward over one batch: router, permute, grouped gate_up GEMM with
 the fused activation, grouped down GEMM and combine (and the shared expert when the
@@ -262,6 +264,38 @@ def time_launches(call, reps: int, stream) -> float:
         b.record(stream)
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+# Equal-row per-expert gate_up shapes (experts, rows per expert, K = H, N = 2F) on which
+# this library's grouped GEMM and the vendor library's batched GEMM (torch.bmm) can run the
+# same product: no gather, no activation, the same operands.
+VENDOR_SHAPES = {"qwen3": (128, 256, 2048, 1536), "dsv3": (256, 128, 7168, 4096)}
+
+
+def compare_vendor(names, reps: int):
+    """moe_grouped_gemm and torch.bmm (hipBLASLt on this image) on the same equal-row expert
+    shapes: a [E*m, K] token rows, b [E, N, K] weights; the vendor call takes b as a
+    contiguous [E, K, N] copy (its right operand must not be a transposed view). HIP events
+    around each launch; one JSON line per shape (a measurement aid, not the bench line)."""
+    s = torch.cuda.current_stream()
+    for name in names:
+        E, m, K, N = VENDOR_SHAPES[name]
+        g = torch.Generator(device="cuda").manual_seed(0)
+        a = torch.randn((E * m, K), device="cuda", generator=g).to(torch.bfloat16)
+        b = (0.02 * torch.randn((E, N, K), device="cuda", generator=g)).to(torch.bfloat16)
+        bt = b.transpose(1, 2).contiguous()
+        off = torch.arange(0, E * m + 1, m, dtype=torch.int32, device="cuda")
+        out = torch.empty((E * m, N), dtype=torch.bfloat16, device="cuda")
+        out_v = torch.empty((E, m, N), dtype=torch.bfloat16, device="cuda")
+        ours = lambda: B.moe_grouped_gemm(a, b, off, None, out=out, stream=s)
+        vendor = lambda: torch.bmm(a.view(E, m, K), bt, out=out_v)
+        t_ours, t_vendor = time_launches(ours, reps, s), time_launches(vendor, reps, s)
+        diff = float((out.view(E, m, N).float() - out_v.float()).abs().max())
+        nbytes = E * N * K * 2 + E * m * K * 2 + E * m * N * 2
+        print(json.dumps({"compare": "grouped GEMM vs vendor batched GEMM", "shape": name,
+                          "experts": E, "rows_per_expert": m, "K": K, "N": N,
+                          "ours_ms": round(t_ours, 4), "vendor_ms": round(t_vendor, 4),
+                          "bytes": nbytes, "max_abs_diff": diff}), flush=True)
 
 
 def time_burst(call, reps: int, stream) -> float:
@@ -684,6 +718,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--compare-vendor", default=None,
+                    help="comma list of " + ",".join(VENDOR_SHAPES) + ": this grouped GEMM "
+                         "and torch.bmm on the same equal-row expert shapes")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured stream-read and MFMA-loop ceilings")
     ap.add_argument("--host-inputs", action="store_true",
@@ -696,6 +733,9 @@ def main(argv=None):
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.compare_vendor:
+        compare_vendor(args.compare_vendor.split(","), args.kernel_reps)
         return
     if args.workload in I.FP8_CONFIGS:
         torch.cuda.set_device(0)
