@@ -293,7 +293,12 @@ static int grouped_gemm_common(const void* a, const int32_t* a_rows, int32_t a_r
   // 16-bit tiles address A and one expert's weights with 32-bit byte offsets
   if (dt != MOE_F32 && (M * Kd * 2 >= ((int64_t)1 << 31) || Nw * Kd * 2 >= ((int64_t)1 << 31)))
     return MOE_ERR_UNSUPPORTED;
-  if (dt == MOE_F32 && Kd > 12288) return MOE_ERR_UNSUPPORTED;  // A row staged in LDS
+  // float32: the tiled kernel (K a multiple of 4, 32-bit byte offsets, 2^24 or more
+  // multiply-adds), else the row-at-a-time kernel, which stages an A row in LDS
+  const int64_t lim32 = (int64_t)1 << 31;
+  const bool f32_tiles = Kd % 4 == 0 && M * Kd * 4 < lim32 && Nw * Kd * 4 < lim32 &&
+                         M * Nw * Kd >= ((int64_t)1 << 24);
+  if (dt == MOE_F32 && !f32_tiles && Kd > 12288) return MOE_ERR_UNSUPPORTED;
   const int64_t Nout = act_on ? Nw / 2 : Nw;
   const size_t s = dt_size(dt);
   const size_t meta_bytes = seg_mode == kSegOffsets ? (size_t)(E + 1) * 4

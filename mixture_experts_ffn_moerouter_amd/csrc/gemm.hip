@@ -68,7 +68,8 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 
 constexpr int kNT = 512;                // 8 waves: 2 (token rows) x 4 (weight rows)
 constexpr int kBNW = 256;               // weight rows per tile
-constexpr int kBK = 64;                 // K elements per step (128 bytes of a row)
+// K elements per step: 128 bytes of a row (dtype 0 float32, else 16-bit)
+constexpr int step_elems(int dt) { return dt == 0 ? 32 : 64; }
 constexpr int kPB = kBNW / 64;          // 1 KB transfers of weight rows per wave and step
 constexpr int kXcd = 8;
 constexpr uint32_t kOOB = 0x80000000u;  // byte offset past every buffer range used here
@@ -111,6 +112,13 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   constexpr int kStage = stage_bytes(BM);
   constexpr int kNI = BM / 32;         // 16-row blocks per wave
   static_assert(BM % 32 == 0 && kNPA <= 8 * kPA, "tile rows");
+  // Element size: 2 bytes (bfloat16, float16) or 4 (float32, DT 0). A step is always 128
+  // bytes of a row, so the transfers and fragment reads are the same for every dtype.
+  constexpr int ES = DT == 0 ? 4 : 2;
+  constexpr int KBK = 128 / ES;        // K elements per step
+  constexpr int EPP = 16 / ES;         // K elements per 16-byte piece
+  constexpr int KS = DT == 0 ? 8 : 2;  // MFMAs per 16 x 16 block and step
+  static_assert(DT != 0 || OUT_F32, "float32 operands give float32 outputs");
   __shared__ int s_tmp[kNT / 64];
   extern __shared__ __align__(16) uint8_t smem[];  // [NS][kStage], then the tile map
   const int E = g.E;
@@ -131,7 +139,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   const int Lend = min((xcd + 1) * per, n_valid);
   if (L0 >= Lend) return;  // uniform per workgroup
   const int ntile = (Lend - L0 + nslot - 1) / nslot;
-  const int Kd = g.Kd, nk = (Kd + kBK - 1) / kBK;
+  const int Kd = g.Kd, nk = (Kd + KBK - 1) / KBK;
 
   // i-th tile of this workgroup: expert, n-tile, rows [m0, m1)
   auto tile = [&](int i, int& e, int& nt, int& m0, int& m1) {
@@ -151,8 +159,8 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   // 32 w + 31); lane l takes row l / 8 of the piece and its 16-byte part (l % 8) ^ (row % 8).
   auto apiece = [&](int u) { return min(kPA * wave + u, kNPA - 1); };
   const int prow = lane >> 3;
-  const int kel = 8 * ((lane & 7) ^ prow);  // first K element of the lane's part
-  const uint32_t pbyte = 2u * (uint32_t)kel;
+  const int kel = EPP * ((lane & 7) ^ prow);  // first K element of the lane's part
+  const uint32_t pbyte = (uint32_t)ES * (uint32_t)kel;
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)g.a, (short)0, 0x7fffffff, 0x00020000);
   // per-lane byte offsets (and the expert's weight buffer) of one tile
@@ -165,11 +173,11 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
       const bool on = r < rows;
       const int m = m0 + (on ? r : 0);
       const int src = g.a_rows ? g.a_rows[m] / g.a_rows_div : m;
-      ao[u] = on ? (uint32_t)src * (uint32_t)Kd * 2u + pbyte : kOOB;
+      ao[u] = on ? (uint32_t)src * (uint32_t)Kd * (uint32_t)ES + pbyte : kOOB;
     }
     rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)g.b + (int64_t)e * g.Nw * Kd), (short)0,
-        (int)((int64_t)g.Nw * Kd * 2), 0x00020000);
+        (void*)((const uint8_t*)g.b + (int64_t)e * g.Nw * Kd * ES), (short)0,
+        (int)((int64_t)g.Nw * Kd * ES), 0x00020000);
 #pragma unroll
     for (int u = 0; u < kPB; ++u) {
       const int b = 8 * (kPB * wave + u) + prow;  // weight row of the tile
@@ -185,7 +193,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         wr = nt * kBNW + b;
         on = wr < g.Nw;
       }
-      bo[u] = on ? (uint32_t)wr * (uint32_t)Kd * 2u + pbyte : kOOB;
+      bo[u] = on ? (uint32_t)wr * (uint32_t)Kd * (uint32_t)ES + pbyte : kOOB;
     }
   };
   int te, tnt, tm0, tm1;              // the tile being multiplied
@@ -196,9 +204,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
   // transfer p of step kk of this tile (nxt false) or the next into stage st
   auto piece = [&](int stage, int kk, bool nxt, int p, auto aux_c) {
     uint8_t* st = smem + stage * kStage;
-    const int k0 = kk * kBK;
+    const int k0 = kk * KBK;
     const bool in = k0 + kel < Kd;
-    const uint32_t kbyte = (uint32_t)k0 * 2u;
+    const uint32_t kbyte = (uint32_t)k0 * (uint32_t)ES;
     if (p < kPA) {
       const uint32_t o = nxt ? aN[p] : aC[p];
       dma16(ra, st + apiece(p) * 1024, in ? o + kbyte : kOOB);
@@ -224,7 +232,11 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
 #pragma unroll
     for (int p = 0; p < kPieces; ++p) piece(q, q, false, p, std::integral_constant<int, 0>{});
 
-  const uint16_t* bias = (const uint16_t*)g.bias;
+  const void* bias = g.bias;
+  auto bias_at = [&](int64_t idx) {
+    if constexpr (DT == 0) return ((const float*)bias)[idx];
+    else return h16_to_f32<DT>(((const uint16_t*)bias)[idx]);
+  };
   const bool aligned = ((uintptr_t)g.out & 15) == 0;
   int gs = 0;  // steps of the earlier tiles (ring position)
   for (int ti = 0; ti < ntile; ++ti) {
@@ -251,7 +263,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     // The K loop, compiled for each count of live 16-row blocks of the wave (1 .. kNI).
     auto main_loop = [&](auto ni_c, auto aux_c) {
       constexpr int NI = decltype(ni_c)::value;
-      constexpr int NB = NI * 8;  // MFMAs per step
+      constexpr int NB = NI * 4 * KS;  // MFMAs per step
       constexpr int EVERY = NB / kPieces;
       static_assert(EVERY >= 1 && EVERY * kPieces <= NB, "every transfer is issued");
       for (int k = 0; k < nk; ++k) {
@@ -287,8 +299,15 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         // MFMA t and, every EVERY-th slot, one transfer of step s + LA (pinned in order)
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-          const int c = t / (NI * 4), u = t % (NI * 4), i = u / 4, j = u % 4;
-          acc[i][j] = mfma16<DT>(fb[j][c], fa[i][c], acc[i][j]);
+          const int ks = t / (NI * 4), u = t % (NI * 4), i = u / 4, j = u % 4;
+          if constexpr (DT == 0) {  // piece c's four floats, one per 16x16x4 MFMA
+            const int c = ks >> 2, x = ks & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                __builtin_bit_cast(f32x4, fb[j][c])[x], __builtin_bit_cast(f32x4, fa[i][c])[x],
+                acc[i][j], 0, 0, 0);
+          } else {
+            acc[i][j] = mfma16<DT>(fb[j][ks], fa[i][ks], acc[i][j]);
+          }
           if (t % EVERY == EVERY - 1 && t / EVERY < kPieces) piece(s2, kk, nxt, t / EVERY, aux_c);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -316,7 +335,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
     // wn 64 + 16 j + 4 q .. + 3.
     auto store4 = [&](int64_t idx, const float* v, bool vec, int n, int nmax) {
       if (vec) {
-        if (OUT_F32) {
+        if constexpr (OUT_F32) {
           *(f32x4*)((float*)g.out + idx) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
           const uint32_t lo =
@@ -329,7 +348,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (n + c < nmax) {
-            if (OUT_F32) ((float*)g.out)[idx + c] = v[c];
+            if constexpr (OUT_F32) ((float*)g.out)[idx + c] = v[c];
             else ((uint16_t*)g.out)[idx + c] = f32_to_h16<DT>(v[c]);
           }
         }
@@ -343,12 +362,12 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         if (o0 < g.Nout) {
           float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
           if (bias) {
-            const uint16_t* be = bias + (int64_t)e * g.Nw;
+            const int64_t be = (int64_t)e * g.Nw;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
               const int o = min(o0 + c, g.Nout - 1);
-              bg[c] = h16_to_f32<DT>(be[LAYOUT == 0 ? o : 2 * o]);
-              bu[c] = h16_to_f32<DT>(be[LAYOUT == 0 ? g.Nout + o : 2 * o + 1]);
+              bg[c] = bias_at(be + (LAYOUT == 0 ? o : 2 * o));
+              bu[c] = bias_at(be + (LAYOUT == 0 ? g.Nout + o : 2 * o + 1));
             }
           }
 #pragma unroll
@@ -375,7 +394,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
           if (bias) {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-              bn[c] = h16_to_f32<DT>(bias[(int64_t)e * g.Nw + min(n0 + c, g.Nw - 1)]);
+              bn[c] = bias_at((int64_t)e * g.Nw + min(n0 + c, g.Nw - 1));
           }
 #pragma unroll
           for (int i = 0; i < kNI; ++i) {
@@ -511,7 +530,7 @@ hipError_t launch_h16_ns(const GemmArgs& g, hipStream_t s) {
 // round weighted by its tile's transfer bytes per step (tile rows + 256).
 template <bool ACT, int LAYOUT, bool OUT_F32, int DT, int TAG = 0>
 hipError_t launch_h16_act(const GemmArgs& g, hipStream_t s) {
-  if (g.Kd <= kBK) return launch_h16_ns<2, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
+  if (g.Kd <= step_elems(DT)) return launch_h16_ns<2, 128, ACT, LAYOUT, OUT_F32, DT, TAG>(g, s);
   bool tall = 3 * stage_bytes(160) + map_bytes(g.E) + kStaticLds <= kLds;
   if (tall && g.seg_mode == kSegOffsets && !g.offsets) {
     const int64_t nt = ACT ? (g.Nout + kBNW / 2 - 1) / (kBNW / 2) : (g.Nw + kBNW - 1) / kBNW;
@@ -530,29 +549,50 @@ static_assert(3 * stage_bytes(128) + map_bytes(1024) + kStaticLds <= kLds, "LDS"
 
 template <int DT>
 hipError_t launch_h16(const GemmArgs& g, hipStream_t s) {
-  if (g.tag == 1 && g.out_dt == g.dt && (!g.act || g.layout == 0))  // the shared expert
-    return g.act ? launch_h16_act<true, 0, false, DT, 1>(g, s)
-                 : launch_h16_act<false, 0, false, DT, 1>(g, s);
-  if (g.act) {
-    if (g.layout == 0)
-      return g.out_dt == 0 ? launch_h16_act<true, 0, true, DT>(g, s)
-                           : launch_h16_act<true, 0, false, DT>(g, s);
-    return g.out_dt == 0 ? launch_h16_act<true, 1, true, DT>(g, s)
-                         : launch_h16_act<true, 1, false, DT>(g, s);
+  if constexpr (DT == 0) {  // float32 operands: float32 outputs only
+    if (g.tag == 1 && (!g.act || g.layout == 0))  // the shared expert
+      return g.act ? launch_h16_act<true, 0, true, 0, 1>(g, s)
+                   : launch_h16_act<false, 0, true, 0, 1>(g, s);
+    if (g.act)
+      return g.layout == 0 ? launch_h16_act<true, 0, true, 0>(g, s)
+                           : launch_h16_act<true, 1, true, 0>(g, s);
+    return launch_h16_act<false, 0, true, 0>(g, s);
+  } else {
+    if (g.tag == 1 && g.out_dt == g.dt && (!g.act || g.layout == 0))  // the shared expert
+      return g.act ? launch_h16_act<true, 0, false, DT, 1>(g, s)
+                   : launch_h16_act<false, 0, false, DT, 1>(g, s);
+    if (g.act) {
+      if (g.layout == 0)
+        return g.out_dt == 0 ? launch_h16_act<true, 0, true, DT>(g, s)
+                             : launch_h16_act<true, 0, false, DT>(g, s);
+      return g.out_dt == 0 ? launch_h16_act<true, 1, true, DT>(g, s)
+                           : launch_h16_act<true, 1, false, DT>(g, s);
+    }
+    return g.out_dt == 0 ? launch_h16_act<false, 0, true, DT>(g, s)
+                         : launch_h16_act<false, 0, false, DT>(g, s);
   }
-  return g.out_dt == 0 ? launch_h16_act<false, 0, true, DT>(g, s)
-                       : launch_h16_act<false, 0, false, DT>(g, s);
+}
+
+// The tiled MFMA kernel takes float32 operands whose rows are whole 16-byte pieces (K a
+// multiple of 4) and whose byte offsets fit 32 bits, once the product has 2^24
+// multiply-adds or more: below that its fixed cost (tile map, ring fill) exceeds the
+// row-at-a-time kernel's whole time (the 64-token float32 layer: 25 against 35 us).
+bool f32_tiles_ok(const GemmArgs& g) {
+  const int64_t lim = (int64_t)1 << 31;
+  return g.Kd % 4 == 0 && (int64_t)g.M * g.Kd * 4 < lim && (int64_t)g.Nw * g.Kd * 4 < lim &&
+         (int64_t)g.M * g.Nw * g.Kd >= ((int64_t)1 << 24);
 }
 
 }  // namespace
 
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0) return hipSuccess;
-  if (g.dt == 0) {
+  if (g.dt == 0 && !f32_tiles_ok(g)) {
     dim3 grid(g.M, (g.Nout + 255) / 256);
     gemm_f32_kernel<<<grid, 256, (size_t)g.Kd * sizeof(float), s>>>(g);
     return hipGetLastError();
   }
+  if (g.dt == 0) return launch_h16<0>(g, s);
   return g.dt == 2 ? launch_h16<2>(g, s) : launch_h16<1>(g, s);
 }
 

@@ -52,6 +52,11 @@ SMALL = {
                              x_std=2.0, w_std=0.1),
     "gelu_like_f32": I.MoEConfig("gelu_like_f32", T=70, H=96, E=12, F=40, K=3, dtype="f32",
                                  act="gelu_and_mul", bias_std=0.1, w_std=0.1),
+    # float32 GEMMs large enough for the tiled kernel (the small float32 cases above take
+    # the row-at-a-time one), with biases, groups and a shared expert
+    "f32_tiled": I.MoEConfig("f32_tiled", T=512, H=256, E=8, F=128, K=2, dtype="f32",
+                             scoring="sigmoid", G=4, TG=2, correction_bias=(-0.1, 0.1),
+                             rsf=2.5, act="swigluoai", bias_std=0.1, w_std=0.05, F_s=128),
     "bf16_logits_groups": I.MoEConfig("bf16_logits_groups", T=256, H=512, E=32, F=128, K=8,
                                       scoring="sigmoid", rsf=2.5, G=8, TG=4,
                                       correction_bias=(-0.1, 0.1), logits_dtype="bf16"),

@@ -95,6 +95,26 @@ def test_grouped_gemm_swiglu(dt, seg, act, gather, H):
         assert np.max(h[:, 0::2]) > 7.0 and np.min(h[:, 1::2]) < -7.0
 
 
+@pytest.mark.parametrize("Kd", [130, 62])
+def test_grouped_gemm_f32_row_kernel(Kd):
+    """float32 with K not a multiple of 4 (rows that are not whole 16-byte pieces) takes the
+    row-at-a-time kernel; the same bound as the tiled one."""
+    sizes = SEGMENTS["ragged"]
+    E, M, N = len(sizes), int(sum(sizes)), 72
+    say(f"[gemm] f32 row kernel K={Kd}")
+    g = torch.Generator(device="cuda").manual_seed(3)
+    a = torch.randn((M, Kd), device="cuda", generator=g)
+    b = 0.1 * torch.randn((E, N, Kd), device="cuda", generator=g)
+    bb = 0.1 * torch.randn((E, N), device="cuda", generator=g)
+    off = _offsets(sizes)
+    out, check = guarded((M, N), torch.float32)
+    B.moe_grouped_gemm(a, b, off, bb, out_dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    check()
+    ref = O.grouped_gemm(np64(a), np64(b), off.cpu().numpy(), np64(bb), "f32")
+    assert_close(np64(out), ref, "f32", "f32 row kernel")
+
+
 def test_gemm_large_expert_rows():
     """Rows beyond 2^16 and offsets starting past row 0."""
     say("[gemm] large M")
