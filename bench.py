@@ -48,16 +48,17 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # their comments and blank lines removed (gemm_source_digest), and different code reports
 # null.
 TRAFFIC = {
-    # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
-    # 524301.2 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
+    # FETCH_SIZE KiB x 1.99994 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
+    # 524302.8 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
     # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
-    # routed gate_up: 8363999.1 + 142723.7 KiB
-    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17275144578,
-                  "gemm_src": "eb43b0aa5c36ea96e3c548fff61ae39d368b773da655c89c025c22821274bcdf"},
-    # routed gate_up: 497489.8 + 50699.8 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1070747478,
-                   "gemm_src": "eb43b0aa5c36ea96e3c548fff61ae39d368b773da655c89c025c22821274bcdf"},
-    # FP8, profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
+    # routed gate_up: 8304425.5 + 143084.6 KiB
+    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17153503720,
+                  "gemm_src": "f4d8ae8cedcbff1152eeff0ef975eb7ca201a86a6a384036e79d2bddb4b70dae"},
+    # routed gate_up: 508024.8 + 50811.3 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1092436298,
+                   "gemm_src": "f4d8ae8cedcbff1152eeff0ef975eb7ca201a86a6a384036e79d2bddb4b70dae"},
+    # FP8 (FETCH_SIZE x 1.99995 from that file's calibration),
+    # profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9308609010,
                          "gemm_src": "4be2967d76e0b9f3a697f64f0aedd7eb041a765278899cb507cc4cf3c577542e"},
     # 1909742.6 + 462315.2 KiB
@@ -459,7 +460,7 @@ def swiglu_line(cfg, args):
         call()
     torch.cuda.synchronize()
     ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    k_ms = time_launches(call, args.kernel_reps, stream)
+    k_ms = time_burst(call, args.kernel_reps, stream)
     es = 4 if cfg.dtype == "f32" else 2
     k_bytes = cfg.rows * cfg.F * 3 * es
     achieved = k_bytes / (k_ms * 1e-3) / 1e9
@@ -495,7 +496,7 @@ def swiglu_line(cfg, args):
     print(json.dumps(line), flush=True)
 
 
-def _timed_line(call, args, stream):
+def _timed_line(call, args, stream, burst: bool = False):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -504,7 +505,8 @@ def _timed_line(call, args, stream):
         call()
     torch.cuda.synchronize()
     ms_per_step = 1e3 * (time.perf_counter() - t0) / args.steps
-    return ms_per_step, time_launches(call, args.kernel_reps, stream)
+    timer = time_burst if burst else time_launches
+    return ms_per_step, timer(call, args.kernel_reps, stream)
 
 
 def layout_line(cfg, args):
@@ -522,7 +524,7 @@ def layout_line(cfg, args):
                          dtype=torch.uint8, device="cuda")
         call = lambda: B.moe_pre_permute(d["hidden"], ids, mc.E, cfg.layout, cfg.block_size,
                                          workspace=ws, stream=stream)
-        ms, k_ms = _timed_line(call, args, stream)
+        ms, k_ms = _timed_line(call, args, stream, burst=True)
         R = mc.T * mc.K
         es = 4 if mc.dtype == "f32" else 2
         k_bytes = mc.T * mc.H * es + R * mc.H * es + R * 4 + R * 4 + mc.E * 4
