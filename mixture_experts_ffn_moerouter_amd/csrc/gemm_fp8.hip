@@ -8,17 +8,21 @@
 //      to a float32 accumulator; the result is stored in bfloat16. Rows at or past m_g
 //      are not written.
 //
-// Tile: 128 token rows x 256 weight rows (two b_scale blocks), eight waves (2 x 4) of 64 x
-// 64, one workgroup per CU. A K step is one 128-wide scale block: 128 bytes of every row.
+// Tile: 160 token rows x 256 weight rows (two b_scale blocks), eight waves (2 x 4): the two
+// row waves take alternate 16-row blocks (80 rows each), the four column waves 64 weight
+// rows each; one workgroup per CU. A K step is one 128-wide scale block: 128 bytes of every
+// row. An expert of up to 160 rows is one row tile, so its weight lines are read once.
 //
 // Staging. Three LDS stages form a ring filled by direct-to-LDS buffer loads (no register
 // staging, no LDS write instructions): step k + 2 is requested while step k is multiplied,
 // so each transfer has two steps to land. One load instruction moves 1 KB, eight rows x
 // 128 bytes (whole cache lines); lane l lands in row l / 8, 16-byte slot l % 8, and fetches
-// the row's byte piece (l % 8) ^ (row % 8), so slots are XOR-swizzled by row. The scales
-// of the step travel the same way (4-byte transfers: a_scale of the tile's rows, the two
-// b_scale blocks). A wave's seven transfers of the next step are spread through its MFMA
-// stream rather than issued at once. The compiler's workgroup barrier would wait for every
+// the row's byte piece (l % 8) ^ (row % 8), so slots are XOR-swizzled by row. The 20
+// token-row transfers of a step are dealt three to a wave (a wave past the 20th repeats
+// it, so every wave issues the same count). The scales of the step travel the same way
+// (4-byte transfers: a_scale of the tile's rows, the two b_scale blocks). A wave's eight
+// transfers of the next step are spread through its MFMA stream rather than issued at
+// once. The compiler's workgroup barrier would wait for every
 // transfer in flight, so the step boundary is an explicit "own transfers of this step
 // landed (vmcnt), own LDS reads done, barrier" sequence.
 //
@@ -32,7 +36,7 @@
 // core fed while the vector unit applies the scales. This is the order the page gives:
 // per-block partial sums from the FP8 values, scaled, then accumulated in float32.
 //
-// Tile map: expert g with m_g rows gets ceil(m_g / 128) row tiles of equal height (rounded
+// Tile map: expert g with m_g rows gets ceil(m_g / 160) row tiles of equal height (rounded
 // up to 32 rows), built on the device from the counts; logical tiles are ordered expert,
 // n-tile, row tile and dealt so that consecutive ones run on one XCD (the row tiles of an
 // expert share its weight lines in that XCD's L2).
@@ -48,16 +52,19 @@ typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kNT = 512;                 // 8 waves: 2 (token rows) x 4 (weight rows)
-constexpr int kBMX = 128;                // token rows per tile
+constexpr int kBMX = 160;                // token rows per tile
 constexpr int kBNW = 256;                // weight rows per tile
 constexpr int kNS = 3;                   // LDS stages
 constexpr int kA = 0;                    // stage layout (bytes): token rows
 constexpr int kB = kA + kBMX * 128;      // weight rows
 constexpr int kSA = kB + kBNW * 128;     // a_scale of the tile's rows
-constexpr int kSB = kSA + kBMX * 4;      // the two b_scale blocks (one 256-byte transfer)
+constexpr int kSB = kSA + 3 * 256;       // the two b_scale blocks (one 256-byte transfer)
 constexpr int kSink = kSB + 256;         // landing area of the idle waves' scale transfer
 constexpr int kStage = kSink + 256;
-constexpr int kPieces = 7;               // transfers per wave and step: 2 A, 4 B, 1 scale
+constexpr int kPA = 3;                   // token-row transfers per wave and step
+constexpr int kNPA = kBMX / 8;           // distinct ones (a wave past them repeats the last)
+constexpr int kPieces = kPA + 5;         // transfers per wave and step: 3 A, 4 B, 1 scale
+constexpr int kNI = kBMX / 32;           // 16-row blocks per wave
 constexpr int kDepth = 2;                // MFMAs between a block's MFMA and its scaling
 constexpr int kMaxE = 1024;
 constexpr int kXcd = 8;
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
   const int rpt = rows_per_tile(cnt, kBMX);
   const int m0 = mt * rpt, m1 = min(m0 + rpt, cnt);
   const int rows = m1 - m0;
-  const int nb = (rows + 31) / 32;
+  const int nb = (rows + 15) / 16;
   __syncthreads();  // every thread has read the map; the buffer becomes the stages
 
   // Buffer resources over expert e's slabs (32-bit offsets within one expert).
@@ -111,15 +118,17 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
       (void*)(g.b_scale + (int64_t)e * (N / 128) * nkb), (short)0, (int)((N / 128) * nkb * 4),
       0x00020000);
 
-  // Wave w moves 1 KB pieces 2w, 2w + 1 of the token tile (rows 16w .. 16w + 15) and
-  // 4w .. 4w + 3 of the weight tile (rows 32w .. 32w + 31). Rows past the tile or the
-  // matrix get an offset past the buffer; what lands for them is never stored.
+  // Wave w moves 1 KB pieces apiece(u) = min(3 w + u, 19) of the token tile (piece q holds
+  // rows 8 q .. 8 q + 7) and 4w .. 4w + 3 of the weight tile (rows 32w .. 32w + 31). Rows
+  // past the tile or the matrix get an offset past the buffer; what lands for them is
+  // never stored.
+  auto apiece = [&](int u) { return min(kPA * wave + u, kNPA - 1); };
   const int prow = lane >> 3;
   const uint32_t pbyte = 16u * (uint32_t)((lane & 7) ^ prow);
-  uint32_t aoff[2], boff[4];
+  uint32_t aoff[kPA], boff[4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int r = 8 * (2 * wave + u) + prow;
+  for (int u = 0; u < kPA; ++u) {
+    const int r = 8 * apiece(u) + prow;
     aoff[u] = r < rows ? (uint32_t)(m0 + r) * (uint32_t)K + pbyte : kOOB;
   }
 #pragma unroll
@@ -127,16 +136,19 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
     const int wr = nt * kBNW + 8 * (4 * wave + u) + prow;
     boff[u] = wr < N ? (uint32_t)wr * (uint32_t)K + pbyte : kOOB;
   }
-  // Scales: waves 0 and 1 move the a_scale of rows 64 w + lane, wave 2 the two b_scale
-  // blocks of the tile; the other waves' transfer is empty (keeps the count uniform).
+  // Scales: waves 0, 1 and 3 move the a_scale of rows 64 s + lane (s = 0, 1, 2; the third
+  // covers rows 128 .. 159, its other lanes land zeros in the region's unused tail), wave
+  // 2 the two b_scale blocks of the tile; the other waves' transfer is empty (keeps the
+  // count uniform).
   uint32_t soff = kOOB;
   __amdgpu_buffer_rsrc_t rs = rsb;
   int sdst = kSink;
-  if (wave < 2) {
-    const int r = 64 * wave + lane;
+  if (wave < 2 || wave == 3) {
+    const int sl = wave == 3 ? 2 : wave;
+    const int r = 64 * sl + lane;
     soff = r < rows ? (uint32_t)(m0 + r) * nkb * 4u : kOOB;
     rs = rsa;
-    sdst = kSA + 256 * wave;
+    sdst = kSA + 256 * sl;
   } else if (wave == 2) {
     const int blk = nt * 2 + lane;
     soff = (lane < 2 && blk < N / 128) ? (uint32_t)blk * nkb * 4u : kOOB;
@@ -147,27 +159,29 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
     uint8_t* st = smem + (kb % kNS) * kStage;
     const bool in = kb < nkb;
     const uint32_t k0 = (uint32_t)kb * 128u;
-    if (p < 2) dma16(ra, st + kA + (2 * wave + p) * 1024, in ? aoff[p] + k0 : kOOB);
-    else if (p < 6) dma16(rb, st + kB + (4 * wave + p - 2) * 1024, in ? boff[p - 2] + k0 : kOOB);
+    if (p < kPA) dma16(ra, st + kA + apiece(p) * 1024, in ? aoff[p] + k0 : kOOB);
+    else if (p < kPA + 4)
+      dma16(rb, st + kB + (4 * wave + p - kPA) * 1024, in ? boff[p - kPA] + k0 : kOOB);
     else dma4(rs, st + sdst, in ? soff + 4u * (uint32_t)kb : kOOB);
   };
 
-  // Wave (wm, wn): token 16-row blocks rowblk(i) = (wm + 2 (i / 2)) 32 + 16 (i % 2), weight
-  // rows wn 64 + 16 j. Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
+  // Wave (wm, wn): token 16-row blocks rowblk(i) = (2 i + wm) 16 (the two row waves take
+  // alternate blocks, so a partly filled tile stays balanced), weight rows wn 64 + 16 j.
+  // Fragment of row r: lane (r % 16, q) takes pieces q and q + 4.
   const int wm = wave & 1, wn = wave >> 1;
   const int lr = lane & 15, lq = lane >> 4;
   const uint32_t fo0 = 16u * (uint32_t)(lq ^ (lr & 7));
   const uint32_t fo1 = 16u * (uint32_t)((lq ^ 4) ^ (lr & 7));
-  auto rowblk = [&](int i) { return (wm + 2 * (i >> 1)) * 32 + 16 * (i & 1); };
-  const int nbw = nb > wm ? (nb - wm + 1) / 2 : 0;  // live 32-row blocks of this wave
+  auto rowblk = [&](int i) { return (2 * i + wm) * 16; };
+  const int nbw = nb > wm ? (nb - wm + 1) / 2 : 0;  // live 16-row blocks of this wave
   auto frag = [&](const uint8_t* rowp) {
     const i32x4 lo = *(const i32x4*)(rowp + fo0), hi = *(const i32x4*)(rowp + fo1);
     return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[kNI][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kNI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
 
@@ -228,7 +242,12 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
     // no transfer into LDS may outlive the workgroup
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  if (nbw >= 2) main_loop(std::integral_constant<int, 4>{});
+  // the K loop for the wave's count of live 16-row blocks (a wave without live rows runs
+  // the smallest instance: its transfers and barriers are the other waves' too)
+  static_assert(kNI == 5, "instances below");
+  if (nbw >= 5) main_loop(std::integral_constant<int, 5>{});
+  else if (nbw == 4) main_loop(std::integral_constant<int, 4>{});
+  else if (nbw == 3) main_loop(std::integral_constant<int, 3>{});
   else main_loop(std::integral_constant<int, 2>{});
 
   // Epilogue: lane (r, q) of block (i, j) holds token row rowblk(i) + r and weight rows
@@ -238,9 +257,9 @@ __global__ __launch_bounds__(kNT, 1) void gemm_fp8_masked_kernel(Fp8GemmArgs g) 
     const int n = nt * kBNW + wn * 64 + 16 * j + 4 * lq;
     if (n < N) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < kNI; ++i) {
         const int m = m0 + rowblk(i) + lr;
-        if (i < 2 * nbw && m < m1) {
+        if (i < nbw && m < m1) {
           const uint32_t lo = (uint32_t)f32_to_bf16(acc[i][j][0]) |
                               ((uint32_t)f32_to_bf16(acc[i][j][1]) << 16);
           const uint32_t hi = (uint32_t)f32_to_bf16(acc[i][j][2]) |
