@@ -58,12 +58,12 @@ TRAFFIC = {
     "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1092436298,
                    "gemm_src": "f4d8ae8cedcbff1152eeff0ef975eb7ca201a86a6a384036e79d2bddb4b70dae"},
     # FP8 (FETCH_SIZE x 1.99995 from that file's calibration),
-    # profiles/gemm_fp8_masked_dsv3_traffic.md: 4413536.2 + 263589.0 KiB
-    "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 9308609010,
-                         "gemm_src": "4be2967d76e0b9f3a697f64f0aedd7eb041a765278899cb507cc4cf3c577542e"},
-    # 1909742.6 + 462315.2 KiB
-    "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4384464964,
-                      "gemm_src": "4be2967d76e0b9f3a697f64f0aedd7eb041a765278899cb507cc4cf3c577542e"},
+    # profiles/gemm_fp8_masked_dsv3_traffic.md: 3791612.6 + 264821.8 KiB
+    "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 8036203622,
+                         "gemm_src": "65476cfa041b9c3bcf1e42f6b5a4464206460bd97f362ac527e192f6c034934e"},
+    # 1895355.4 + 484635.7 KiB
+    "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4377856522,
+                      "gemm_src": "65476cfa041b9c3bcf1e42f6b5a4464206460bd97f362ac527e192f6c034934e"},
 }
 
 

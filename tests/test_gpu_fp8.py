@@ -68,8 +68,11 @@ def test_fp8_small_all_counts():
     check(got, ref, h["counts"], cfg.K, cfg.name)
 
 
+# (E, max_m, K, N), counts from max_m down to 1: 320 / 160 / 1 rows are two full 160-row
+# tiles, one full tile and one row; 161 rows are two tiles (96 + 65)
 @pytest.mark.parametrize("shape", [(1, 32, 128, 128), (3, 96, 256, 128), (2, 300, 640, 384),
-                                   (4, 128, 1024, 256)])  # (E, max_m, K, N)
+                                   (4, 128, 1024, 256), (3, 320, 384, 256),
+                                   (2, 161, 256, 384)])
 def test_fp8_shapes(shape):
     E, max_m, K, N = shape
     say(f"[fp8] shape {shape}")
