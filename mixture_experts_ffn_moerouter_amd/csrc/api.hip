@@ -87,6 +87,8 @@ struct FfnWs {
   size_t topk_w, topk_ids, offsets, sorted, pos, active, blk_cnt, act, y, shared_act, total;
 };
 
+int backend_for(const moe_ffn_cfg& c, bool has_bias);
+
 FfnWs ffn_ws_layout(const moe_ffn_cfg& c) {
   FfnWs w;
   const size_t R = (size_t)c.T * c.route.top_k, E = (size_t)c.E, s = dt_size(c.dtype);
@@ -99,8 +101,13 @@ FfnWs ffn_ws_layout(const moe_ffn_cfg& c) {
   w.active = o; o += align256((E + 1) * 4);
   w.blk_cnt = o; o += align256(permute_workspace_bytes((int)R, (int)E));
   w.act = o; o += align256(R * (size_t)c.F * s);
-  const size_t y_elt = s > 4 ? s : 4;  // the indexed backend keeps y in float32
-  w.y = o; o += align256(R * (size_t)c.H * y_elt);
+  // the indexed backend (when the configuration can take it: biases rule it out, so the
+  // bias-free choice decides) keeps y in float32, one slab per chunk of its down contraction
+  const size_t y_staged = R * (size_t)c.H * s;
+  const size_t y_indexed = backend_for(c, false) == MOE_BACKEND_INDEXED
+                               ? (size_t)indexed_down_chunks(c.F) * R * (size_t)c.H * 4
+                               : 0;
+  w.y = o; o += align256(y_staged > y_indexed ? y_staged : y_indexed);
   w.shared_act = o; o += align256((size_t)c.T * (size_t)c.F_shared * s);
   w.total = o;
   return w;
@@ -639,7 +646,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
                                      backend == MOE_BACKEND_INDEXED ? active : nullptr,
                                      (int32_t*)(ws + w.blk_cnt), strm))))
     return st;
-  int y_dt = c.dtype;
+  int y_dt = c.dtype, y_chunks = 1;
   if (backend == MOE_BACKEND_INDEXED) {
     IndexedArgs ia;
     ia.hidden = (const uint16_t*)hidden;
@@ -658,6 +665,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
     ia.y = (float*)y;
     if ((st = status_of(launch_indexed_mlp(ia, strm)))) return st;
     y_dt = MOE_F32;
+    y_chunks = indexed_down_chunks((int)F);
   } else {
     // 3. gate_up GEMM + activation, A rows gathered from hidden by route
     GemmArgs g;
@@ -701,7 +709,7 @@ int moe_ffn_forward(const moe_ffn_cfg* cfg, const void* hidden, const void* logi
   }
   // 5. weighted combine (routed_scaling_factor is already in the weights)
   if ((st = status_of(launch_combine(y, y_dt, topk_w, pos, (int)T, (int)K, (int)H, 1.0f, out,
-                                     c.dtype, strm))))
+                                     c.dtype, strm, y_chunks, (int64_t)R * H))))
     return st;
   // 6. shared expert: one "expert" owning every token
   if (c.F_shared > 0) {

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ route_pos,
                                                       int T, int K, int H, float scale,
-                                                      void* out, int out_dt) {
+                                                      void* out, int out_dt, int nchunk,
+                                                      int64_t chunk_stride) {
   const int t = blockIdx.x;
   if (t >= T) return;
   const float* wt = w + (int64_t)t * K;
@@ -54,6 +55,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
         if (pt[k] < 0) continue;  // a route without a row contributes nothing
         float v[8];
         load8<YDT>((const char*)y + ((int64_t)pt[k] * H + h) * ysz, v);
+        if constexpr (YDT == 0) {  // partial slabs of a split contraction, in order
+          for (int c = 1; c < nchunk; ++c) {
+            float u[8];
+            load8<YDT>((const float*)y + c * chunk_stride + (int64_t)pt[k] * H + h, u);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] += u[i];
+          }
+        }
         const float wk = wt[k];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
@@ -77,7 +86,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
       float acc = 0.f;
       for (int k = 0; k < K; ++k) {
         if (pt[k] < 0) continue;
-        const float v = load_dt(y, YDT, (int64_t)pt[k] * H + h);
+        float v = load_dt(y, YDT, (int64_t)pt[k] * H + h);
+        if constexpr (YDT == 0)
+          for (int c = 1; c < nchunk; ++c)
+            v += ((const float*)y)[c * chunk_stride + (int64_t)pt[k] * H + h];
         acc = fmaf(wt[k], v, acc);
       }
       store_dt(out, out_dt, (int64_t)t * H + h, scale * acc);
@@ -89,15 +101,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
 
 hipError_t launch_combine(const void* y, int y_dt, const float* w, const int32_t* route_pos,
                           int T, int K, int H, float scale, void* out, int out_dt,
-                          hipStream_t s) {
+                          hipStream_t s, int nchunk, int64_t chunk_stride) {
+  if (nchunk > 1 && y_dt != 0) return hipErrorInvalidValue;
   if (T <= 0 || H <= 0) return hipSuccess;
   const bool vec = (H % 8) == 0;
   const dim3 grid(T, (H + kChunk - 1) / kChunk);
 #define MOE_COMBINE(D)                                                                        \
   (vec ? combine_kernel<D, true><<<grid, kThreads, 0, s>>>(y, w, route_pos, T, K, H, scale, out, \
-                                                           out_dt)                             \
+                                                           out_dt, nchunk, chunk_stride)       \
        : combine_kernel<D, false><<<grid, kThreads, 0, s>>>(y, w, route_pos, T, K, H, scale, out, \
-                                                            out_dt))
+                                                            out_dt, nchunk, chunk_stride))
   if (y_dt == 0) MOE_COMBINE(0);
   else if (y_dt == 1) MOE_COMBINE(1);
   else MOE_COMBINE(2);

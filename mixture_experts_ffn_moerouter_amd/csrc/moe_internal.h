@@ -142,9 +142,15 @@ struct GemmArgs {
 };
 hipError_t launch_grouped_gemm(const GemmArgs& g, hipStream_t s);
 
+// y may hold nchunk partial slabs ([nchunk][rows][H], float32 only when nchunk > 1), added
+// in slab order before the route weight is applied.
 hipError_t launch_combine(const void* y, int y_dt, const float* w, const int32_t* route_pos,
                           int T, int K, int H, float scale, void* out, int out_dt,
-                          hipStream_t s);
+                          hipStream_t s, int nchunk = 1, int64_t chunk_stride = 0);
+
+// The indexed backend's down projection splits the contraction into chunks of 512
+// elements when F allows (each chunk's partial sums form one float32 y slab).
+__host__ __device__ inline int indexed_down_chunks(int F) { return F % 512 == 0 ? F / 512 : 1; }
 
 // Indexed small-route backend (bf16 or f16, silu_and_mul, no bias).
 struct IndexedArgs {
@@ -157,7 +163,7 @@ struct IndexedArgs {
   int T, H, E, F, K;
   int dt;                     // 1 bf16, 2 f16
   uint16_t* act;              // [R, F] workspace (permuted rows)
-  float* y;                   // [R, H] workspace (permuted rows)
+  float* y;                   // [indexed_down_chunks(F)][R, H] workspace (permuted rows)
 };
 hipError_t launch_indexed_mlp(const IndexedArgs& a, hipStream_t s);
 

@@ -78,11 +78,21 @@ def test_backend_choice_follows_dispatch_rule(name):
 
 
 def test_workspace_size_covers_buffers():
+    # staged backend: act and y in the operand dtype
     cfg = I.CONFIGS["dsv3_bf16"]
+    assert B.moe_ffn_backend(B.ffn_cfg(cfg), False) == 1
     ws = B.moe_ffn_workspace_size(B.ffn_cfg(cfg))
     R = cfg.T * cfg.K
-    assert ws >= R * cfg.F * 2 + R * cfg.H * 4 + cfg.T * cfg.F_s * 2
+    assert ws >= R * cfg.F * 2 + R * cfg.H * 2 + cfg.T * cfg.F_s * 2
     assert ws % 256 == 0
+    # indexed backend: y in float32, one slab per 512-element chunk of the down contraction
+    dec = I.CONFIGS["decode_dsv3_bf16"]
+    assert B.moe_ffn_backend(B.ffn_cfg(dec), False) == 2
+    R = dec.T * dec.K
+    chunks = dec.F // 512 if dec.F % 512 == 0 else 1
+    assert chunks == 4
+    assert B.moe_ffn_workspace_size(B.ffn_cfg(dec)) >= \
+        R * dec.F * 2 + chunks * R * dec.H * 4 + dec.T * dec.F_s * 2
     bad = B.ffn_cfg(cfg.with_(E=250))     # E % G != 0
     assert B.moe_ffn_workspace_size(bad) == 0
     assert B.moe_ffn_backend(bad, False) == -1
