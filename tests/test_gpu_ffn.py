@@ -35,8 +35,13 @@ SMALL = {
     "decode_like_indexed": I.MoEConfig("decode_like_indexed", T=16, H=256, E=64, F=256, K=4,
                                        scoring="sigmoid", G=4, TG=2,
                                        correction_bias=(-0.1, 0.1), rsf=2.5),
-    "decode_many_routes_per_expert": I.MoEConfig("decode_many", T=40, H=384, E=24, F=512,
+    # the decode backend's down contraction in chunks of 512: three here (and three passes
+    # over one expert's routes in test_indexed_passes_over_route_groups), two below
+    "decode_many_routes_per_expert": I.MoEConfig("decode_many", T=40, H=384, E=24, F=1536,
                                                  K=1, renormalize=False),
+    "decode_like_indexed_chunks": I.MoEConfig("decode_like_indexed_chunks", T=16, H=256,
+                                              E=64, F=1024, K=4, scoring="sigmoid", G=4, TG=2,
+                                              correction_bias=(-0.1, 0.1), rsf=2.5),
     "single_token": I.MoEConfig("single_token", T=1, H=128, E=4, F=64, K=2),
     # a per-expert logit ramp: some experts take most tokens, many take none
     "skewed_load": I.MoEConfig("skewed_load", T=600, H=320, E=48, F=192, K=6, logit_skew=6.0),
