@@ -9,7 +9,9 @@
 // One workgroup per token and chunk of kChunk hidden elements (several per token when H is
 // large, so small batches still spread over the chip); each thread owns 8 consecutive
 // elements (16-byte loads of 16-bit rows, non-temporal: each expert output is read once),
-// sums its K rows in float32 in k order and writes once.
+// sums its K rows in float32 in k order and writes once. A float32 y may come as partial
+// slabs of a split contraction (the decode backend's down projection): a route's slabs are
+// added in slab order before its weight is applied.
 #include "moe_internal.h"
 
 namespace moe {

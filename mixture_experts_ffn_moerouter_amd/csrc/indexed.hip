@@ -8,8 +8,8 @@
 // With a handful of routes per expert the work is a stream of the touched experts'
 // weights, so the kernels are built around reading weight rows at full HBM rate:
 //   * A wave owns 32 weight rows (gate_up: 16 gate rows and the 16 matching up rows;
-//     down: 32 rows of W_d) and streams them over the whole contraction in 256-byte
-//     blocks. Each load instruction reads 4 rows x 256 contiguous bytes (16 lanes per
+//     down: 32 rows of W_d) and streams them over the contraction (down: one chunk of
+//     it, below) in 256-byte blocks. Each load instruction reads 4 rows x 256 contiguous bytes (16 lanes per
 //     row), whole cache lines, the pattern that streams at full rate.
 //   * MFMA operands need the opposite layout (a lane holds 8 contraction elements of ONE
 //     row), so each block goes through a wave-private LDS tile: the wave writes the
