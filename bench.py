@@ -64,6 +64,10 @@ TRAFFIC = {
     # 1895355.4 + 484635.7 KiB
     "dsv3_fp8_down": {"kernel": "gemm_fp8.hip", "bytes": 4377856522,
                       "gemm_src": "65476cfa041b9c3bcf1e42f6b5a4464206460bd97f362ac527e192f6c034934e"},
+    # decode: one whole layer call (router, permute, both indexed kernels, combine),
+    # profiles/moe_ffn_decode_dsv3_bf16_traffic.md: 4010184.5 + 15080.7 KiB
+    "decode_dsv3_bf16": {"kernel": ("indexed.hip", "combine.hip"), "bytes": 8228095172,
+                         "gemm_src": "c827bb773a1a558a5b6f378761cb902fb7c9aeb254ff5f3738fd81839692bc73"},
 }
 
 
@@ -75,11 +79,11 @@ def code_text(src: str) -> str:
     return "\n".join(line for line in lines if line)
 
 
-def gemm_source_digest(kernel: str = "gemm.hip") -> str:
-    """SHA-256 over the code of a GEMM kernel's source and the tile-map header it includes
-    (comments do not count: editing one leaves the recorded figures valid)."""
+def gemm_source_digest(kernel="gemm.hip") -> str:
+    """SHA-256 over the code of a kernel's source (or a tuple of sources) and the tile-map
+    header (comments do not count: editing one leaves the recorded figures valid)."""
     h = hashlib.sha256()
-    for name in (kernel, "tile_map.h"):
+    for name in ((kernel,) if isinstance(kernel, str) else tuple(kernel)) + ("tile_map.h",):
         with open(os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "csrc", name)) as f:
             h.update(code_text(f.read()).encode())
     return h.hexdigest()
@@ -801,7 +805,7 @@ def main(argv=None):
         k_bytes = l_bytes
         k_flops = l_flops
         k_name = "moe_ffn_forward, indexed backend (indexed_kernel gate_up + down dominate)"
-        k_traffic = None
+        k_traffic = recorded_traffic(cfg.name)
     # the binding roof of the timed kernel: MFMA above the ridge, HBM below it
     if k_flops / k_bytes > RIDGE:
         roof = {"bound": "mfma", "achieved": round(k_flops / (k_ms * 1e-3) / 1e12, 1),
