@@ -271,10 +271,11 @@ def time_launches(call, reps: int, stream) -> float:
     return float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-# Equal-row per-expert gate_up shapes (experts, rows per expert, K = H, N = 2F) on which
-# this library's grouped GEMM and the vendor library's batched GEMM (torch.bmm) can run the
-# same product: no gather, no activation, the same operands.
-VENDOR_SHAPES = {"qwen3": (128, 256, 2048, 1536), "dsv3": (256, 128, 7168, 4096)}
+# Equal-row per-expert shapes (experts, rows per expert, K, N) on which this library's
+# grouped GEMM and the vendor library's batched GEMM (torch.bmm) can run the same product:
+# no gather, no activation, the same operands. gate_up: K = H, N = 2F; down: K = F, N = H.
+VENDOR_SHAPES = {"qwen3": (128, 256, 2048, 1536), "dsv3": (256, 128, 7168, 4096),
+                 "qwen3_down": (128, 256, 768, 2048), "dsv3_down": (256, 128, 2048, 7168)}
 
 
 def compare_vendor(names, reps: int):
