@@ -840,8 +840,8 @@ def main(argv=None):
                   "algorithmic_bytes": l_bytes, "flops": l_flops,
                   "distinct_experts": n_exp},
     }
-    # the benchmark spec's targets: 60 % of bf16 MFMA peak for prefill layers, 70 % of HBM
-    # bandwidth for decode layers (whole-layer fractions, next to the target)
+    # the layer's fraction beside its target: 60 % of bf16 MFMA peak for prefill layers,
+    # 70 % of HBM bandwidth for decode layers
     if backend == "staged":
         line["layer_mfma_frac"] = line["layer"]["mfma_frac"]
         line["mfma_target"] = 0.60
