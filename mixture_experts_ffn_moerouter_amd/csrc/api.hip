@@ -469,18 +469,11 @@ int moe_pre_permute(const void* hidden, int64_t T, int64_t H, int32_t dt,
     return status_of(launch_masked_rows(hidden, (int64_t)row, (int)K, (int)R, off, sorted,
                                         (int)E, (int)max_m, expert_input, layout_metadata,
                                         inverse_indices, s));
-  int32_t* padded = (int32_t*)(ws + w.padded);
-  int32_t* sorted_ids = (int32_t*)(ws + w.sorted_ids);
-  int32_t* expert_blk = (int32_t*)(ws + w.expert_blk);
-  st = status_of(launch_align(off, sorted, (int)R, (int)E, (int)bs, padded, sorted_ids,
-                              expert_blk, nullptr,
-                              layout == MOE_LAYOUT_CONTIGUOUS ? layout_metadata : nullptr, s));
-  if (st) return st;
-  return status_of(launch_contiguous_rows(hidden, (int64_t)row, (int)K, sorted_ids, expert_blk,
-                                          padded, (int)E, (int)bs, (int)R, (int)cap,
-                                          expert_input, inverse_indices,
-                                          layout == MOE_LAYOUT_PER_ROW ? layout_metadata : nullptr,
-                                          s));
+  return status_of(launch_align_rows(hidden, (int64_t)row, (int)K, off, sorted, (int)E, (int)bs,
+                                     (int)cap, expert_input, inverse_indices,
+                                     layout == MOE_LAYOUT_PER_ROW ? layout_metadata : nullptr,
+                                     layout == MOE_LAYOUT_CONTIGUOUS ? layout_metadata : nullptr,
+                                     s));
 }
 
 int moe_grouped_gemm_fp8_masked(const void* a, const float* a_scale, const void* b,

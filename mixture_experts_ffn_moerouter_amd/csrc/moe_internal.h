@@ -102,11 +102,12 @@ __host__ __device__ inline int align_len(int R, int E, int bs) { return R + (E +
 hipError_t launch_align(const int32_t* off, const int32_t* sorted_route, int R, int E, int bs,
                         int32_t* padded_off, int32_t* sorted_ids, int32_t* expert_blk,
                         int32_t* num_post_pad, int32_t* seg_ends, hipStream_t s);
-hipError_t launch_contiguous_rows(const void* hidden, int64_t row_bytes, int K,
-                                  const int32_t* sorted_ids, const int32_t* expert_blk,
-                                  const int32_t* padded_off, int E, int bs, int R, int cap,
-                                  void* out, int32_t* inverse, int32_t* row_ids,
-                                  hipStream_t s);
+// Contiguous / per-row pre-permute with the align step fused in (from the tight permute's
+// offsets and order): rows, inverse indices, per-row expert ids and/or segment ends.
+hipError_t launch_align_rows(const void* hidden, int64_t row_bytes, int K, const int32_t* off,
+                             const int32_t* sorted_route, int E, int bs, int cap, void* out,
+                             int32_t* inverse, int32_t* row_ids, int32_t* seg_ends,
+                             hipStream_t s);
 hipError_t launch_masked_rows(const void* hidden, int64_t row_bytes, int K, int R,
                               const int32_t* off, const int32_t* sorted_route, int E,
                               int max_m, void* out, int32_t* counts, int32_t* inverse,
