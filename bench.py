@@ -781,6 +781,17 @@ def main(argv=None):
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
     tokens_per_s = cfg.T * args.steps / elapsed
+    # the spread of single steps, from HIP events around each layer in a second pass (the
+    # timed region above has no events in it)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in evs:
+        a.record(stream)
+        run_layer(cfg, d, fcfg, ws, out, shared_out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_ms = [a.elapsed_time(b) for a, b in evs]
 
     _, ids, _, _ = B.moe_route(d["logits"], B.route_cfg(cfg.K, cfg.scoring, cfg.renormalize,
                                                         cfg.rsf, cfg.G, cfg.TG),
@@ -823,6 +834,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(np.min(step_ms)), 4), "source": "HIP events per step"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
