@@ -536,7 +536,7 @@ def layout_line(cfg, args):
         value, unit = R / (ms * 1e-3), "routes/s"
         conf = {"workload": cfg.name, "T": mc.T, "top_k": mc.K, "E": mc.E, "H": mc.H,
                 "layout": cfg.layout, "block_size": cfg.block_size}
-        kernel = "permute + align + contiguous_rows_kernel (the whole op)"
+        kernel = "permute + align_rows_kernel (the whole op)"
         dtype = mc.dtype
         sample = None
         if not args.no_cpu_baseline:
