@@ -204,7 +204,7 @@ def coverage_tokens(topk_ids: np.ndarray, E: int, stride: int = 32) -> np.ndarra
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_ffn_full_size(name):
+def test_ffn_full_size_every_expert(name):
     cfg = I.CONFIGS[name]
     say(f"[ffn-full] {name} generating inputs")
     d = I.make_inputs(cfg, device="cuda")
