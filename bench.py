@@ -705,11 +705,20 @@ def cpu_baseline(cfg, d, budget_s: float):
     while total < budget_s / 2:  # whole workload is quick: repeat it to about 10 s
         total += run(n)
         passes += 1
-    return {"value": n * passes / total, "unit": "tokens/s", **host_description(threads),
-            "kind": "oracle",
-            "sample": f"first {n} of {cfg.T} tokens of the same workload, {passes} pass(es), "
-                      f"float64 C oracle (oracle/moe_ref.c) on {threads} threads, "
-                      f"{total:.1f} s wall"}
+    res = {"value": n * passes / total, "unit": "tokens/s", **host_description(threads),
+           "kind": "oracle",
+           "sample": f"first {n} of {cfg.T} tokens of the same workload, {passes} pass(es), "
+                     f"float64 C oracle (oracle/moe_ref.c) on {threads} threads, "
+                     f"{total:.1f} s wall"}
+    if cfg.T <= 64 and threads > 1:
+        # small batches (the tiny and decode layers): the whole batch on one thread too
+        C1, t0 = load(1), time.perf_counter()
+        C1.moe_ffn_forward(host["hidden"], host["logits"], host["w_gate_up"], host["w_down"],
+                           expert_ids=ids, **kw)
+        wall = time.perf_counter() - t0
+        res["single_thread"] = {"value": cfg.T / wall, "unit": "tokens/s",
+                                "wall_s": round(wall, 3), "sample": f"all {cfg.T} tokens"}
+    return res
 
 
 def main(argv=None):
