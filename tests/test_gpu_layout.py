@@ -27,7 +27,7 @@ def _ids(T, K, E, seed, hot=None):
 
 @pytest.mark.parametrize("T,K,E,bs", [(100, 4, 8, 16), (1, 1, 4, 64), (4096, 8, 128, 64),
                                       (37, 3, 7, 1), (0, 2, 5, 4), (513, 6, 256, 5),
-                                      (64, 8, 16, 128)])
+                                      (64, 8, 16, 128), (2000, 8, 1024, 4), (3, 2, 1024, 16)])
 def test_permute_align(T, K, E, bs):
     say(f"[align] T={T} K={K} E={E} bs={bs}")
     ids = _ids(T, K, E, 1, hot=E - 1)
@@ -66,6 +66,32 @@ def test_pre_permute(dt, layout, arg):
     assert np.array_equal(got_rows, want_rows)
     if layout == "masked" and arg == 40:
         assert (inv_o < 0).any()  # the hot expert overflowed its slab
+
+
+# The contiguous and per-row forms run the align step inside the row copy: the largest
+# expert count the LDS prefix holds (1024, four experts per thread), rows whose bytes are not
+# whole 16-byte pieces (the byte path), rows of several 4 KB rounds, an empty batch whose
+# layout is all padding, and a grid whose last workgroup is partly past the rows.
+@pytest.mark.parametrize("T,K,E,H,dt,layout,bs", [
+    (2000, 8, 1024, 64, "bf16", "contiguous", 4), (50, 2, 1024, 24, "f32", "per_row", 16),
+    (300, 4, 12, 7, "bf16", "contiguous", 8), (300, 4, 12, 7, "bf16", "per_row", 1),
+    (512, 8, 64, 7168, "bf16", "contiguous", 64), (0, 4, 16, 64, "bf16", "per_row", 8),
+    (3, 1, 1, 40, "f32", "contiguous", 1)])
+def test_pre_permute_shapes(T, K, E, H, dt, layout, bs):
+    say(f"[pre-permute] T={T} K={K} E={E} H={H} dt={dt} layout={layout} bs={bs}")
+    g = torch.Generator(device="cuda").manual_seed(4)
+    hidden = torch.randn((T, H), device="cuda", generator=g).to(DT[dt])
+    ids = _ids(T, K, E, 5, hot=E - 1)
+    x, meta, inv = B.moe_pre_permute(hidden, ids, E, layout, block_size=bs)
+    torch.cuda.synchronize()
+    xo, meta_o, inv_o = O.pre_permute(np64(hidden), ids.cpu().numpy(), E, layout,
+                                      block_size=bs)
+    assert np.array_equal(meta.cpu().numpy(), meta_o)
+    assert np.array_equal(inv.cpu().numpy(), inv_o)
+    if T:
+        live = torch.as_tensor(inv_o, device="cuda").long()
+        want = hidden[torch.arange(T * K, device="cuda") // K]
+        assert np.array_equal(_row_bits(x[live]), _row_bits(want))
 
 
 def _offsets_rows(sizes):
