@@ -74,6 +74,10 @@ SMALL = {
     "decode_max_experts": I.MoEConfig("decode_max_experts", T=64, H=128, E=512, F=256, K=8,
                                       scoring="sigmoid", G=8, TG=4,
                                       correction_bias=(-0.1, 0.1), rsf=2.5),
+    # a shared expert of DeepSeek-V3-like size (M 4096, K 4096 and 2048, N 4096): every
+    # token of its dense GEMMs compared, where the full-size layer test samples tokens
+    "shared_dense_tiles": I.MoEConfig("shared_dense_tiles", T=4096, H=4096, E=8, F=64, K=2,
+                                      F_s=2048),
 }
 
 
