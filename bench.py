@@ -145,10 +145,12 @@ def host_description(cores: int = 0) -> dict:
 
 
 def measured_ceilings(reps: int = 5) -> dict:
-    """The device's attainable streaming-read bandwidth and dense bf16 MFMA rate, from the
-    probes of libmoe_probes.so (include/moe_probes.h), timed with HIP events on the
-    current stream: a 4 GiB read with non-temporal 16-byte loads, and four independent
-    v_mfma_f32_32x32x16_bf16 chains per wave at two waves per SIMD. Best of `reps`."""
+    """The device's attainable streaming-read bandwidth, L2-resident read rate and dense
+    bf16 MFMA rate, from the probes of libmoe_probes.so (include/moe_probes.h), timed with
+    HIP events on the current stream: a 4 GiB read with non-temporal 16-byte loads; a 1 MiB
+    region read 4096 times per wave by one eight-wave workgroup per CU, in both load forms;
+    four independent v_mfma_f32_32x32x16_bf16 chains per wave at two waves per SIMD. Best of
+    `reps`."""
     path = os.path.join(ROOT, "mixture_experts_ffn_moerouter_amd", "libmoe_probes.so")
     L = ctypes.CDLL(path)
     L.moe_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
@@ -168,6 +170,19 @@ def measured_ceilings(reps: int = 5) -> dict:
         assert rc == 0, rc
 
     t_read = min(time_launches(read, 1, stream) for _ in range(reps))
+    # L2-resident reads (a 1 MiB region), one workgroup of eight waves per CU
+    L.moe_probe_l2_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    region, rounds = 1 << 20, 256
+    l2 = {}
+    for name, to_lds in (("lds", 1), ("registers", 0)):
+        def l2read():
+            rc = L.moe_probe_l2_read(buf.data_ptr(), region, rounds, to_lds, sink.data_ptr(),
+                                     cus, sh)
+            assert rc == 0, rc
+        t = min(time_launches(l2read, 1, stream) for _ in range(reps))
+        l2[name] = cus * 512 * 16 * 16 * rounds / (t * 1e-3)
     del buf
     iters = 20000
     mgrid = cus * 2  # 2 workgroups of four waves per CU: two waves per SIMD
@@ -181,8 +196,11 @@ def measured_ceilings(reps: int = 5) -> dict:
     flops = mgrid * 4 * iters * 4 * 2 * 32 * 32 * 16
     return {"hbm_read_GBs": round(nbytes / (t_read * 1e-3) / 1e9, 1),
             "mfma_bf16_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 1),
-            "source": "probes/ceilings.hip (4 GiB non-temporal streaming read; bf16 32x32x16 "
-                      "MFMA loop)"}
+            "l2_read_to_lds_GBs": round(l2["lds"] / 1e9, 1),
+            "l2_read_to_registers_GBs": round(l2["registers"] / 1e9, 1),
+            "source": "probes/ceilings.hip (4 GiB non-temporal streaming read; 1 MiB "
+                      "L2-resident region read by one 8-wave workgroup per CU, 16-byte loads "
+                      "direct to LDS or into registers; bf16 32x32x16 MFMA loop)"}
 
 
 def log(*a):

@@ -287,7 +287,7 @@ def test_probe_library_exports_its_symbols():
     hdr = os.path.join(os.path.dirname(HEADER), "moe_probes.h")
     text = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
     names = sorted(set(re.findall(r"^\s*int\s+(moe_probe_\w+)\s*\(", text, re.M)))
-    assert names == ["moe_probe_mfma_bf16", "moe_probe_stream_read"], names
+    assert names == ["moe_probe_l2_read", "moe_probe_mfma_bf16", "moe_probe_stream_read"], names
     path = os.path.join(os.path.dirname(B.LIB_PATH), "libmoe_probes.so")
     L = ctypes.CDLL(path)
     for n in names:
@@ -300,6 +300,12 @@ def test_probe_library_exports_its_symbols():
     assert L.moe_probe_stream_read(None, 1024, None, 1, None) == 1
     assert L.moe_probe_stream_read(16, 1000, 16, 1, None) == 1
     assert L.moe_probe_mfma_bf16(0, 16, 1, None) == 1
+    L.moe_probe_l2_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_void_p]
+    assert L.moe_probe_l2_read(None, 1 << 20, 1, 1, 16, 1, None) == 1
+    assert L.moe_probe_l2_read(16, 1000, 1, 1, 16, 1, None) == 1  # not whole 1 KB pieces
+    assert L.moe_probe_l2_read(16, 1 << 20, 0, 0, 16, 1, None) == 1
 
 
 def test_noalloc_refuses_a_workspace_beyond_its_scratch():
