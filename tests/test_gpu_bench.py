@@ -48,6 +48,8 @@ def test_bench_line_with_oracle_baseline(capsys, workload):
     assert CPU <= set(cpu), CPU - set(cpu)
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1
     assert cpu["unit"] == line["unit"]
+    if workload == "tiny_fp32":  # a small batch also reports the whole batch on one thread
+        assert cpu["single_thread"]["value"] > 0
 
 
 @pytest.mark.parametrize("workload", ["qwen3_bf16", "qwen3_pre_permute_bs64"])
@@ -60,7 +62,11 @@ def test_bench_line_full_size(capsys, workload):
         assert line["mfma_target"] == 0.60 and 0 < line["layer_mfma_frac"] < 1
         c = line["ceilings"]
         assert 1000 < c["hbm_read_GBs"] < 8000 and 500 < c["mfma_bf16_TFLOPs"] < 2600
+        # L2-resident reads run well above the HBM read ceiling, in either load form
+        assert c["l2_read_to_lds_GBs"] > c["hbm_read_GBs"]
+        assert c["l2_read_to_registers_GBs"] > c["hbm_read_GBs"]
         assert line["roofline"]["measured_ceiling"] > 0
+        assert line["step_ms"]["min"] <= line["step_ms"]["median"]
 
 
 def test_bench_refuses_several_gpus(capsys):
