@@ -48,15 +48,15 @@ METRIC = "MoE FFN tokens/s on 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (de
 # their comments and blank lines removed (gemm_source_digest), and different code reports
 # null.
 TRAFFIC = {
-    # FETCH_SIZE KiB x 1.99994 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
-    # 524302.8 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
+    # FETCH_SIZE KiB x 1.99995 + WRITE_SIZE KiB x 1.0 per launch (a 1 GiB copy read
+    # 524301.3 KiB of FETCH_SIZE and wrote 1048576 KiB of WRITE_SIZE); layer inputs made on
     # the host (--host-inputs), profiles/gemm_<workload>_counters.md.
-    # routed gate_up: 8304425.5 + 143084.6 KiB
-    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17153503720,
-                  "gemm_src": "f4d8ae8cedcbff1152eeff0ef975eb7ca201a86a6a384036e79d2bddb4b70dae"},
-    # routed gate_up: 508024.8 + 50811.3 KiB
-    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1092436298,
-                   "gemm_src": "f4d8ae8cedcbff1152eeff0ef975eb7ca201a86a6a384036e79d2bddb4b70dae"},
+    # routed gate_up: 8376167.2 + 131072.0 KiB
+    "dsv3_bf16": {"kernel": "gemm.hip", "bytes": 17288173022,
+                  "gemm_src": "03eac19500d1e52b478a194bde0c3de9c1c9c7a68b1c6da5293a6db0b16a6c5d"},
+    # routed gate_up: 526729.7 + 49152.1 KiB
+    "qwen3_bf16": {"kernel": "gemm.hip", "bytes": 1129046837,
+                   "gemm_src": "03eac19500d1e52b478a194bde0c3de9c1c9c7a68b1c6da5293a6db0b16a6c5d"},
     # FP8 (FETCH_SIZE x 1.99995 from that file's calibration),
     # profiles/gemm_fp8_masked_dsv3_traffic.md: 3791612.6 + 264821.8 KiB
     "dsv3_fp8_gate_up": {"kernel": "gemm_fp8.hip", "bytes": 8036203622,

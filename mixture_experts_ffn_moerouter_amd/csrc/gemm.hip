@@ -37,9 +37,17 @@
 // q + 4 of row r (both operands alike, so products pair as in the plain sum); with the
 // XOR slots these reads are free of bank conflicts. Each 16 x 16 block takes two
 // v_mfma_f32_16x16x32 per step, weights as the first operand, so a lane's four results
-// are four consecutive outputs of one token row: one 8-byte store (16 in float32). The K
-// loop is compiled once per count of a wave's live 16-row blocks, so a partly filled tile
-// issues no MFMA for blocks that hold only padding.
+// are four consecutive outputs of one token row. The K loop is compiled once per count of
+// a wave's live 16-row blocks, so a partly filled tile issues no MFMA for blocks that
+// hold only padding.
+//
+// Epilogue. 16-bit outputs whose rows are whole 16-byte pieces are gathered through the
+// stage the last step read (its refill is sent only after the next tile's first barrier):
+// each wave writes its results there, and after a barrier the workgroup stores whole
+// tile rows (256 or 512 bytes) as non-temporal 16-byte pieces. A gated tile always fits
+// the stage; a non-gated tile's rows are twice as wide, so it is gathered when its live
+// rows are at most half the tile height. Other tiles store each lane's four results as
+// one 8-byte store (16 in float32).
 //
 // Cache policy. A tile of an expert that has one row tile reads each of its weight lines
 // once, so that tile's weight transfers are non-temporal; an expert with more row tiles
@@ -354,7 +362,82 @@ __global__ __launch_bounds__(kNT, 1) void gemm_h16_kernel(GemmArgs g) {
         }
       }
     };
-    if (ACT) {
+    // Gathered epilogue (16-bit outputs whose rows are whole 16-byte pieces): the tile's
+    // outputs go through the stage the last step read, whose refill is sent only after the
+    // next tile's first barrier, and leave as non-temporal runs of a whole tile row
+    // (writes inside the weight stream cost up to half as much that way as the waves' own
+    // 32-byte pieces). A non-gated tile's rows are twice as wide, so only the
+    // first half of its rows fits the stage: such tiles of more rows store as before.
+    bool gathered = false;
+    if constexpr (!OUT_F32 && DT != 0)
+      gathered = ((ACT ? g.Nout : g.Nw) & 7) == 0 && aligned &&
+                 (ACT || m1 - m0 <= BM / 2);
+    if constexpr (!OUT_F32 && DT != 0) {
+      if (gathered) {
+        constexpr int W = ACT ? kBNW / 2 : kBNW;  // outputs per tile row
+        constexpr int PITCH = 2 * W + 16;         // LDS bytes per tile row
+        constexpr int RR = ACT ? BM : BM / 2;     // tile rows that can be live
+        constexpr int LPR = 2 * W / 16;           // lanes per row, 16 bytes each
+        constexpr int RPI = 64 / LPR;             // rows per store instruction
+        constexpr int NU = RR / (8 * RPI);        // store instructions per wave and round
+        static_assert(RR % (8 * RPI) == 0 && RR % 16 == 0, "gathered rows");
+        static_assert(RR * PITCH <= kStage, "a round fits the stage");
+        const int NO = ACT ? g.Nout : g.Nw;
+        uint8_t* lo = smem + ((gs - 1) % NS) * kStage;
+        // every wave's fragment reads of that stage are done
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        {
+#pragma unroll
+          for (int jj = 0; jj < (ACT ? 2 : 4); ++jj) {
+            const int cl = ACT ? wn * 32 + 16 * jj + 4 * lq : wn * 64 + 16 * jj + 4 * lq;
+            const int c0 = nt * W + cl;  // output column
+            float b0[4] = {0.f, 0.f, 0.f, 0.f}, b1[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias && c0 < NO) {
+              const int64_t be = (int64_t)e * g.Nw;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int o = min(c0 + c, NO - 1);
+                if (ACT) {
+                  b0[c] = bias_at(be + (LAYOUT == 0 ? o : 2 * o));
+                  b1[c] = bias_at(be + (LAYOUT == 0 ? g.Nout + o : 2 * o + 1));
+                } else {
+                  b0[c] = bias_at(be + o);
+                }
+              }
+            }
+#pragma unroll
+            for (int i = 0; i < kNI; ++i) {
+              const int r0 = rowblk(i);
+              if (i < nbw && r0 < RR) {
+                float v[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                  v[c] = ACT ? gated_f(g.act_kind, acc[i][jj][c] + b0[c],
+                                       acc[i][jj + 2][c] + b1[c], g.alpha, g.beta, g.limit)
+                             : acc[i][jj][c] + b0[c];
+                const uint32_t w0 =
+                    (uint32_t)f32_to_h16<DT>(v[0]) | ((uint32_t)f32_to_h16<DT>(v[1]) << 16);
+                const uint32_t w1 =
+                    (uint32_t)f32_to_h16<DT>(v[2]) | ((uint32_t)f32_to_h16<DT>(v[3]) << 16);
+                *(uint2*)(lo + (r0 + lr) * PITCH + 2 * cl) = make_uint2(w0, w1);
+              }
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            const int lrow = (wave * NU + u) * RPI + lane / LPR, chunk = lane % LPR;
+            const int m = m0 + lrow, col = nt * W + 8 * chunk;
+            if (m < m1 && col < NO) {
+              const i32x4 v = *(const i32x4*)(lo + lrow * PITCH + 16 * chunk);
+              __builtin_nontemporal_store(v, (i32x4*)((uint16_t*)g.out + (int64_t)m * NO + col));
+            }
+          }
+        }
+      }
+    }
+    if (gathered) {
+    } else if (ACT) {
       const bool vrow = (g.Nout & 3) == 0 && aligned;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
